@@ -1,0 +1,222 @@
+/*
+ * moe.h -- C ABI of libmoe: an MI355X (gfx950) implementation of a sparse
+ * MoE block with an int8 router, int4 affine group-64 SwiGLU experts carrying
+ * an unmerged LoRA delta, a weighted combine, and a Prerouter head.
+ *
+ * Sources (page title, section):
+ *   [P1] "Edge0开源框架实现35BMoE模型在Mac上流式推理，峰值内存仅2.9GiB"
+ *        (tech.news18a.com): Recover-LoRA paragraph; Prerouter paragraph
+ *        (prediction, expert loading and LoRA delta as separate native parts).
+ *   [P2] "SSD 专家卸载 · Prerouter 路由预测" (autoark.ai): tier table (E, K,
+ *        layers); prefill/decode paragraph; expert-pool and double-shift
+ *        paragraphs.
+ *   [P3] "iPhone、Mac、Android、Windows 实测横评：Edge0 五大平台谁最能打"
+ *        (2kiu.com): model-structure paragraph (256 experts, K=4, hidden
+ *        2048); "三件套" bullets (affine 4-bit, group_size 64; unmerged
+ *        LoRA; prediction heads); quality section (8-bit router gate and
+ *        shared-expert gate).
+ *
+ * Conventions for every entry point:
+ *   - Tensors are row-major.  bf16 values travel as uint16_t bit patterns.
+ *   - "device" pointers must be HIP device memory (or device-visible pinned
+ *     host memory where stated); "host" pointers are ordinary host memory.
+ *   - The caller owns every buffer.  No call allocates or frees device
+ *     memory; scratch comes from the caller's workspace (`ws`, sized by
+ *     moe_workspace_bytes).  Workspace contents need no initialisation.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work on it; nothing synchronises with the host, so every call
+ *     can be captured in a HIP graph.
+ *   - Errors: arguments are validated before anything is enqueued.  A bad
+ *     argument returns MOE_EINVAL, a shape the kernels are not built for
+ *     returns MOE_EUNSUPPORTED, a too-small workspace returns MOE_EWORKSPACE,
+ *     a failed launch returns MOE_EHIP.  moe_last_error() then describes the
+ *     failure (thread-local).  Device faults surface at the caller's next
+ *     synchronisation.  No C++ exception crosses this ABI.
+ *   - Shapes supported by the kernels: H and I in {64, 128, 256, 512, 1024,
+ *     2048, 4096}, 1 <= K <= E <= 1024, K <= 16, 0 <= r <= 32, n_shared in
+ *     {0, 1}; the shared expert has the same shape (H, I, r) as the routed
+ *     ones.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,
+  MOE_EUNSUPPORTED = 2,
+  MOE_EHIP = 3,
+  MOE_EWORKSPACE = 4
+} moe_status_t;
+
+/* Description of the last failure on this thread ("" if none). */
+MOE_API const char* moe_last_error(void);
+
+/* Block dimensions.  [P2] tier table, [P3] model-structure paragraph.
+ *   H  hidden size            E  routed experts     K  experts per token
+ *   I  expert intermediate    r  LoRA rank (0 = no LoRA)
+ *   lora_scale  lambda = alpha / r of the unmerged delta lambda * B (A v)
+ *   n_shared    0 or 1 shared expert gated by sigmoid(shared-gate logit)
+ *   norm_topk   1: weights = softmax over the K selected logits (a full
+ *               softmax renormalised over the selection); 0: plain full-
+ *               softmax entries of the selection. */
+typedef struct {
+  int32_t H, I, E, K, r, n_shared, norm_topk;
+  float lora_scale;
+} moe_dims_t;
+
+/* ---------------------------------------------------------------------------
+ * Expert blobs.  One expert = one contiguous, fixed-stride blob holding
+ * {gate, up, down} x {int4 codes, bf16 scale, bf16 bias} and the LoRA
+ * factors {A, B} x {gate, up, down}; [P3] "三件套" bullets give the affine
+ * 4-bit group-64 format and the unmerged LoRA.  One blob is one expert-pool
+ * slot.  The byte layout inside a blob is private to this library: build
+ * blobs only with moe_pack_expert.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of one expert blob (a multiple of 256). */
+MOE_API size_t moe_expert_blob_bytes(int32_t H, int32_t I, int32_t r);
+
+/* Host-only.  Pack one expert's logical tensors into `blob_out` (host, at
+ * least moe_expert_blob_bytes bytes).  For p in gate, up (out = I, in = H)
+ * and down (out = H, in = I):
+ *   q_p  uint8  [out, in]     codes 0..15 (values above 15 -> MOE_EINVAL)
+ *   s_p  bf16   [out, in/64]  scale, b_p bf16 [out, in/64] bias:
+ *        w[j, i] = s[j, i/64] * q[j, i] + b[j, i/64]
+ *   A_p  bf16   [r, in],  B_p bf16 [out, r]  (may be NULL when r == 0)  */
+MOE_API moe_status_t moe_pack_expert(int32_t H, int32_t I, int32_t r,
+                             const uint8_t* q_gate, const uint16_t* s_gate, const uint16_t* b_gate,
+                             const uint16_t* A_gate, const uint16_t* B_gate,
+                             const uint8_t* q_up, const uint16_t* s_up, const uint16_t* b_up,
+                             const uint16_t* A_up, const uint16_t* B_up,
+                             const uint8_t* q_down, const uint16_t* s_down, const uint16_t* b_down,
+                             const uint16_t* A_down, const uint16_t* B_down,
+                             void* blob_out, size_t blob_bytes);
+
+/* Where the routed experts of one layer live.  [P2] expert-pool paragraph:
+ * a pool caches recently used experts and prefetched ones; here the pool is a
+ * set of HBM slots addressed through a device table.
+ *   slots           device, n_slots blobs of moe_expert_blob_bytes each.
+ *   expert_to_slot  device int32 [E]: slot holding expert e, or -1 if not
+ *                   resident.  NULL means slots holds all E experts in
+ *                   expert order (n_slots == E).
+ *   host_blobs      device-visible pointer to pinned, mapped host memory
+ *                   with all E blobs in expert order; a non-resident expert
+ *                   is read from here over PCIe.  Required when
+ *                   expert_to_slot is not NULL.
+ *   counters        device uint64 [2] or NULL: counters[0] += lookups served
+ *                   from a slot, counters[1] += all lookups. */
+typedef struct {
+  const void* slots;
+  int32_t n_slots;
+  const int32_t* expert_to_slot;
+  const void* host_blobs;
+  unsigned long long* counters;
+} moe_experts_t;
+
+/* Workspace bytes needed by moe_route + moe_expert_forward (+ prefill
+ * grouping when `prefill` != 0) for T tokens.  One workspace may be reused by
+ * consecutive calls on the same stream. */
+MOE_API size_t moe_workspace_bytes(const moe_dims_t* d, int32_t T, int32_t prefill);
+
+/* ---------------------------------------------------------------------------
+ * moe_route: router logits, top-K selection, routing weights, shared gate,
+ * and (optionally) grouping of the (token, k) pairs by expert for prefill.
+ * [P2] tier table / [P3] model-structure paragraph: top-K of E experts per
+ * token; [P3] quality section: 8-bit router gate and shared-expert gate;
+ * [P2] prefill/decode paragraph: prefill batches tokens per expert.
+ *   gate_q  device int8 [E, H], gate_s device fp32 [E, H/64]:
+ *           logit[t, e] = sum_i gate_s[e, i/64] * gate_q[e, i] * x[t, i]
+ *                         (+ logit_bias[e])
+ *   sgate_q device int8 [H], sgate_s fp32 [H/64]: shared-gate projection;
+ *           required iff n_shared == 1.
+ *   x       device bf16 [T, H].      logit_bias  device fp32 [E] or NULL.
+ *   topk_idx  device int32 [T, K]: experts ordered by (-logit, index), so
+ *             equal logits go to the lower index.
+ *   topk_w    device fp32 [T, K]: routing weights (see norm_topk).
+ *   shared_w  device fp32 [T] (n_shared == 1, else may be NULL):
+ *             sigmoid(shared-gate logit).
+ *   logits    device fp32 [T, E] or NULL: the biased logits.
+ *   counts    device int32 [E], offsets int32 [E+1], perm int32 [T*K]: all
+ *             NULL, or all set to group the pairs p = t*K + k by expert
+ *             (offsets exclusive prefix of counts; perm lists each expert's
+ *             pairs in ascending p).  Requires a workspace sized with
+ *             prefill != 0.
+ * T == 0 is valid and enqueues nothing. */
+MOE_API moe_status_t moe_route(const moe_dims_t* d, const int8_t* gate_q, const float* gate_s,
+                       const int8_t* sgate_q, const float* sgate_s, const uint16_t* x,
+                       int32_t T, const float* logit_bias, int32_t* topk_idx, float* topk_w,
+                       float* shared_w, float* logits, int32_t* counts, int32_t* offsets,
+                       int32_t* perm, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_forward: every selected expert's SwiGLU FFN with its unmerged
+ * LoRA delta, plus the shared expert.  [P1] Recover-LoRA paragraph, [P3]
+ * "三件套" bullets: frozen int4 base plus an unmerged LoRA added on the fly.
+ *   a_p = deq(Q_p) v + lora_scale * B_p (A_p v) for p in gate, up, down;
+ *   h = silu(a_gate(x)) * a_up(x);  y = a_down(h)   (h is rounded to bf16).
+ *   routed       where the routed experts live (see moe_experts_t).
+ *   shared_blob  device blob of the shared expert (n_shared == 1) or NULL.
+ *   x            device bf16 [T, H];  topk_idx device int32 [T, K].
+ *   counts, offsets, perm: NULL -> decode path (weight-streaming GEMV, one
+ *                pass over each selected expert per token); the outputs of
+ *                moe_route's grouping -> prefill path (grouped MFMA GEMM
+ *                over each expert's tokens).
+ *   y            device fp32 [T, K + n_shared, H]: y[t, k] is the output of
+ *                expert topk_idx[t, k] on token t; y[t, K] the shared one.
+ */
+MOE_API moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_experts_t* routed,
+                                const void* shared_blob, const uint16_t* x, int32_t T,
+                                const int32_t* topk_idx, const int32_t* counts,
+                                const int32_t* offsets, const int32_t* perm, float* y,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_combine: out[t] = bf16( sum_k topk_w[t,k] y[t,k] + shared_w[t] y[t,K]
+ *                             (+ residual[t]) ).
+ * With `norm_out` set it also writes bf16(RMSNorm(out[t])) (unit gain, eps)
+ * -- the next layer's input in a residual + RMSNorm stack.
+ *   y device fp32 [T, K+n_shared, H]; topk_w fp32 [T, K]; shared_w fp32 [T]
+ *   (n_shared == 1); residual bf16 [T, H] or NULL; out bf16 [T, H];
+ *   norm_out bf16 [T, H] or NULL. */
+MOE_API moe_status_t moe_combine(const moe_dims_t* d, const float* y, const float* topk_w,
+                         const float* shared_w, int32_t T, const uint16_t* residual,
+                         uint16_t* out, uint16_t* norm_out, float eps, void* stream);
+
+/* moe_rmsnorm: out[t] = bf16(h[t] / sqrt(mean(h[t]^2) + eps)), unit gain.
+ * h, out device bf16 [T, H] (may alias). */
+MOE_API moe_status_t moe_rmsnorm(const uint16_t* h, int32_t T, int32_t H, float eps, uint16_t* out,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------
+ * prerouter_predict: the Prerouter head.  [P1] Prerouter paragraph and [P2]
+ * double-shift paragraph: a light MLP after layer N predicts layer N+1's
+ * top-K (for the next token) so expert loads can start early.
+ *   z = W2 silu(W1 h), pred = top-K of z ordered by (-z, index).
+ *   W1 device bf16 [D, H], W2 bf16 [E, D], h bf16 [T, H];
+ *   pred_idx int32 [T, K]; pred_logits fp32 [T, E] or NULL.
+ *   ws: at least prerouter_workspace_bytes(D, E, T) bytes.
+ *   Supported: H as above, D a multiple of 64 up to 4096, 1 <= K <= 16,
+ *   K <= E <= 1024. */
+MOE_API size_t prerouter_workspace_bytes(int32_t D, int32_t E, int32_t T);
+MOE_API moe_status_t prerouter_predict(const uint16_t* W1, const uint16_t* W2, int32_t H, int32_t D,
+                               int32_t E, int32_t K, const uint16_t* h, int32_t T,
+                               int32_t* pred_idx, float* pred_logits, void* ws, size_t ws_bytes,
+                               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,179 @@
+"""ctypes binding of libmoe (argument marshalling only).
+
+Each function has the name of the C entry point it calls and takes torch
+tensors (device memory) or None; it passes raw pointers and sizes through
+and raises MoeError on a non-OK status.  Every step of the computation runs
+in the HIP kernels of libmoe.so; there is no fallback path: if the library
+is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime that libmoe shares (same soname)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+c_i32, c_f32, c_sz, c_vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EHIP", 4: "MOE_EWORKSPACE"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class MoeDims(ctypes.Structure):
+    _fields_ = [("H", c_i32), ("I", c_i32), ("E", c_i32), ("K", c_i32), ("r", c_i32),
+                ("n_shared", c_i32), ("norm_topk", c_i32), ("lora_scale", c_f32)]
+
+
+class MoeExperts(ctypes.Structure):
+    _fields_ = [("slots", c_vp), ("n_slots", c_i32), ("expert_to_slot", c_vp),
+                ("host_blobs", c_vp), ("counters", c_vp)]
+
+
+_lib = None
+
+# name -> (restype, argtypes)
+_SIGS = {
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_expert_blob_bytes": (c_sz, [c_i32, c_i32, c_i32]),
+    "moe_pack_expert": (c_i32, [c_i32, c_i32, c_i32] + [c_vp] * 15 + [c_vp, c_sz]),
+    "moe_workspace_bytes": (c_sz, [ctypes.POINTER(MoeDims), c_i32, c_i32]),
+    "moe_route": (c_i32, [ctypes.POINTER(MoeDims), c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp,
+                          c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "moe_expert_forward": (c_i32, [ctypes.POINTER(MoeDims), ctypes.POINTER(MoeExperts), c_vp,
+                                   c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "moe_combine": (c_i32, [ctypes.POINTER(MoeDims), c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp,
+                            c_f32, c_vp]),
+    "moe_rmsnorm": (c_i32, [c_vp, c_i32, c_i32, c_f32, c_vp, c_vp]),
+    "prerouter_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32]),
+    "prerouter_predict": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp,
+                                  c_vp, c_vp, c_sz, c_vp]),
+}
+
+# symbols the public header declares (checked by the CPU test suite)
+HEADER_SYMBOLS = [
+    "moe_last_error", "moe_expert_blob_bytes", "moe_pack_expert", "moe_workspace_bytes",
+    "moe_route", "moe_expert_forward", "moe_combine", "moe_rmsnorm",
+    "prerouter_workspace_bytes", "prerouter_predict",
+]
+
+
+def load(path: str = LIB_PATH):
+    """Load libmoe.so; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is not built; run `python -m int4_expert_ffn_int8_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        if not hasattr(lib, name):
+            continue
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load().moe_last_error().decode(errors="replace")
+        raise MoeError(status, msg)
+
+
+def ptr(t) -> int | None:
+    """Raw address of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def stream_ptr(stream=None) -> int:
+    """hipStream_t of a torch stream (None -> torch's current stream; an int is
+    taken as a raw handle, 0 = the default stream)."""
+    if isinstance(stream, int):
+        return stream
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def dims(H, I, E, K, r, n_shared, lora_scale=1.0, norm_topk=1) -> MoeDims:
+    return MoeDims(H, I, E, K, r, n_shared, norm_topk, lora_scale)
+
+
+def moe_expert_blob_bytes(H: int, I: int, r: int) -> int:
+    return int(load().moe_expert_blob_bytes(H, I, r))
+
+
+def moe_workspace_bytes(d: MoeDims, T: int, prefill: bool) -> int:
+    return int(load().moe_workspace_bytes(ctypes.byref(d), T, int(bool(prefill))))
+
+
+def moe_pack_expert(H, I, r, ex: dict, out) -> None:
+    """Pack numpy logical tensors of one expert into `out` (host numpy uint8)."""
+    import numpy as np
+    args = []
+    keep = []
+    for p in ("gate", "up", "down"):
+        for k in ("q", "s", "b", "A", "B"):
+            a = np.ascontiguousarray(ex[f"{k}_{p}"])
+            keep.append(a)
+            args.append(a.ctypes.data if a.size else None)
+    assert out.flags["C_CONTIGUOUS"]
+    _check(load().moe_pack_expert(H, I, r, *args, out.ctypes.data, out.nbytes))
+
+
+def moe_route(d, gate_q, gate_s, sgate_q, sgate_s, x, T, logit_bias, topk_idx, topk_w,
+              shared_w, logits, counts, offsets, perm, ws, stream=None) -> None:
+    _check(load().moe_route(ctypes.byref(d), ptr(gate_q), ptr(gate_s), ptr(sgate_q),
+                            ptr(sgate_s), ptr(x), T, ptr(logit_bias), ptr(topk_idx),
+                            ptr(topk_w), ptr(shared_w), ptr(logits), ptr(counts),
+                            ptr(offsets), ptr(perm), ptr(ws),
+                            ws.numel() * ws.element_size() if ws is not None else 0,
+                            stream_ptr(stream)))
+
+
+def experts_struct(slots, n_slots, expert_to_slot=None, host_blobs=None,
+                   counters=None) -> MoeExperts:
+    return MoeExperts(ptr(slots), n_slots, ptr(expert_to_slot), ptr(host_blobs), ptr(counters))
+
+
+def moe_expert_forward(d, routed: MoeExperts, shared_blob, x, T, topk_idx, counts, offsets,
+                       perm, y, ws, stream=None) -> None:
+    _check(load().moe_expert_forward(ctypes.byref(d), ctypes.byref(routed), ptr(shared_blob),
+                                     ptr(x), T, ptr(topk_idx), ptr(counts), ptr(offsets),
+                                     ptr(perm), ptr(y), ptr(ws),
+                                     ws.numel() * ws.element_size() if ws is not None else 0,
+                                     stream_ptr(stream)))
+
+
+def moe_combine(d, y, topk_w, shared_w, T, residual, out, norm_out=None, eps=1e-6,
+                stream=None) -> None:
+    _check(load().moe_combine(ctypes.byref(d), ptr(y), ptr(topk_w), ptr(shared_w), T,
+                              ptr(residual), ptr(out), ptr(norm_out), eps, stream_ptr(stream)))
+
+
+def moe_rmsnorm(h, T, H, eps, out, stream=None) -> None:
+    _check(load().moe_rmsnorm(ptr(h), T, H, eps, ptr(out), stream_ptr(stream)))
+
+
+def prerouter_workspace_bytes(D: int, E: int, T: int) -> int:
+    return int(load().prerouter_workspace_bytes(D, E, T))
+
+
+def prerouter_predict(W1, W2, H, D, E, K, h, T, pred_idx, pred_logits, ws, stream=None) -> None:
+    _check(load().prerouter_predict(ptr(W1), ptr(W2), H, D, E, K, ptr(h), T, ptr(pred_idx),
+                                    ptr(pred_logits), ptr(ws),
+                                    ws.numel() * ws.element_size() if ws is not None else 0,
+                                    stream_ptr(stream)))

@@ -1,0 +1,163 @@
+// C ABI entry points: argument validation, workspace layout, launches.
+#include <math.h>
+#include <string.h>
+
+#include "launch.h"
+#include "moe_internal.h"
+#include "status.h"
+#include "workspace.h"
+
+using namespace moe;
+
+extern "C" const char* moe_last_error(void) { return last_error_buffer(); }
+
+namespace {
+
+moe_status_t check_dims(const moe_dims_t* d, const char* fn) {
+  if (!d) return fail(MOE_EINVAL, "%s: dims is NULL", fn);
+  if (d->H <= 0 || d->I <= 0 || d->H % kGroup || d->I % kGroup)
+    return fail(MOE_EINVAL, "%s: H=%d and I=%d must be positive multiples of 64", fn, d->H, d->I);
+  if (!width_supported(d->H) || !width_supported(d->I))
+    return fail(MOE_EUNSUPPORTED, "%s: H=%d / I=%d not in {64,...,4096} powers of two", fn, d->H,
+                d->I);
+  if (d->E < 1 || d->E > kMaxE)
+    return fail(MOE_EUNSUPPORTED, "%s: E=%d outside [1, %d]", fn, d->E, kMaxE);
+  if (d->K < 1 || d->K > d->E) return fail(MOE_EINVAL, "%s: K=%d outside [1, E=%d]", fn, d->K, d->E);
+  if (d->K > kMaxK) return fail(MOE_EUNSUPPORTED, "%s: K=%d above %d", fn, d->K, kMaxK);
+  if (d->r < 0 || d->r > kMaxR)
+    return fail(MOE_EUNSUPPORTED, "%s: LoRA rank r=%d outside [0, %d]", fn, d->r, kMaxR);
+  if (d->n_shared != 0 && d->n_shared != 1)
+    return fail(MOE_EINVAL, "%s: n_shared=%d must be 0 or 1", fn, d->n_shared);
+  if (d->norm_topk != 0 && d->norm_topk != 1)
+    return fail(MOE_EINVAL, "%s: norm_topk=%d must be 0 or 1", fn, d->norm_topk);
+  if (!isfinite(d->lora_scale)) return fail(MOE_EINVAL, "%s: lora_scale is not finite", fn);
+  return MOE_OK;
+}
+
+moe_status_t hip_status(hipError_t e, const char* fn) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_EHIP, "%s: %s", fn, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" size_t moe_workspace_bytes(const moe_dims_t* d, int32_t T, int32_t prefill) {
+  if (check_dims(d, "moe_workspace_bytes") != MOE_OK || T < 0) return 0;
+  return ws_layout(*d, T, prefill != 0).total;
+}
+
+extern "C" moe_status_t moe_route(const moe_dims_t* d, const int8_t* gate_q, const float* gate_s,
+                                  const int8_t* sgate_q, const float* sgate_s, const uint16_t* x,
+                                  int32_t T, const float* logit_bias, int32_t* topk_idx,
+                                  float* topk_w, float* shared_w, float* logits, int32_t* counts,
+                                  int32_t* offsets, int32_t* perm, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  const char* fn = "moe_route";
+  moe_status_t st = check_dims(d, fn);
+  if (st != MOE_OK) return st;
+  if (T < 0) return fail(MOE_EINVAL, "%s: T=%d is negative", fn, T);
+  const int ngroup = (counts != nullptr) + (offsets != nullptr) + (perm != nullptr);
+  if (ngroup != 0 && ngroup != 3)
+    return fail(MOE_EINVAL, "%s: counts, offsets and perm must be all NULL or all set", fn);
+  const bool group = ngroup == 3;
+  if (T == 0) return MOE_OK;
+  if (!gate_q || !gate_s || !x || !topk_idx || !topk_w)
+    return fail(MOE_EINVAL, "%s: null gate, x or output pointer", fn);
+  if (d->n_shared && (!sgate_q || !sgate_s || !shared_w))
+    return fail(MOE_EINVAL, "%s: n_shared=1 needs sgate_q, sgate_s and shared_w", fn);
+  const WsLayout W = ws_layout(*d, T, group);
+  if (!ws || ws_bytes < W.total)
+    return fail(MOE_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, W.total);
+  if (group) return fail(MOE_EUNSUPPORTED, "%s: prefill grouping not built yet", fn);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  float* lg = logits ? logits : reinterpret_cast<float*>(wsb + W.logits);
+  float* sg = reinterpret_cast<float*>(wsb + W.sg);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(launch_router_logits(d->H, gate_q, gate_s, sgate_q, sgate_s, x, logit_bias, d->E,
+                                       d->n_shared, T, lg, sg, s),
+                  fn);
+  if (st != MOE_OK) return st;
+  return hip_status(
+      launch_topk(lg, sg, T, d->E, d->K, d->n_shared, d->norm_topk, topk_idx, topk_w, shared_w, s),
+      fn);
+}
+
+extern "C" moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_experts_t* routed,
+                                           const void* shared_blob, const uint16_t* x, int32_t T,
+                                           const int32_t* topk_idx, const int32_t* counts,
+                                           const int32_t* offsets, const int32_t* perm, float* y,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_expert_forward";
+  moe_status_t st = check_dims(d, fn);
+  if (st != MOE_OK) return st;
+  if (T < 0) return fail(MOE_EINVAL, "%s: T=%d is negative", fn, T);
+  const int ngroup = (counts != nullptr) + (offsets != nullptr) + (perm != nullptr);
+  if (ngroup != 0 && ngroup != 3)
+    return fail(MOE_EINVAL, "%s: counts, offsets and perm must be all NULL or all set", fn);
+  const bool group = ngroup == 3;
+  if (!routed || !routed->slots) return fail(MOE_EINVAL, "%s: routed experts missing", fn);
+  if (routed->expert_to_slot == nullptr && routed->n_slots < d->E)
+    return fail(MOE_EINVAL, "%s: without a slot table n_slots=%d must cover E=%d experts", fn,
+                routed->n_slots, d->E);
+  if (routed->expert_to_slot != nullptr && routed->host_blobs == nullptr)
+    return fail(MOE_EINVAL, "%s: a slot table needs host_blobs for non-resident experts", fn);
+  if (routed->n_slots < 1) return fail(MOE_EINVAL, "%s: n_slots=%d", fn, routed->n_slots);
+  if (d->n_shared && !shared_blob) return fail(MOE_EINVAL, "%s: n_shared=1 needs shared_blob", fn);
+  if (T == 0) return MOE_OK;
+  if (!x || !topk_idx || !y) return fail(MOE_EINVAL, "%s: null x, topk_idx or y", fn);
+  const WsLayout W = ws_layout(*d, T, group);
+  if (!ws || ws_bytes < W.total)
+    return fail(MOE_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, W.total);
+  if (group) return fail(MOE_EUNSUPPORTED, "%s: prefill path not built yet", fn);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  DecodeArgs a;
+  a.x = x;
+  a.topk_idx = topk_idx;
+  a.T = T;
+  a.H = d->H;
+  a.I = d->I;
+  a.K = d->K;
+  a.S = d->n_shared;
+  a.r = d->r;
+  a.lam = d->lora_scale;
+  a.L = blob_layout(d->H, d->I, d->r);
+  a.src.slots = static_cast<const uint8_t*>(routed->slots);
+  a.src.expert_to_slot = routed->expert_to_slot;
+  a.src.host_blobs = static_cast<const uint8_t*>(routed->host_blobs);
+  a.src.counters = routed->counters;
+  a.src.stride = a.L.total;
+  a.shared_blob = static_cast<const uint8_t*>(shared_blob);
+  a.blobptr = reinterpret_cast<unsigned long long*>(wsb + W.blobptr);
+  a.u = reinterpret_cast<float*>(wsb + W.u);
+  a.h = reinterpret_cast<uint16_t*>(wsb + W.h);
+  a.vpart = reinterpret_cast<float*>(wsb + W.vpart);
+  a.y = y;
+  return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+extern "C" moe_status_t moe_combine(const moe_dims_t* d, const float* y, const float* topk_w,
+                                    const float* shared_w, int32_t T, const uint16_t* residual,
+                                    uint16_t* out, uint16_t* norm_out, float eps, void* stream) {
+  const char* fn = "moe_combine";
+  moe_status_t st = check_dims(d, fn);
+  if (st != MOE_OK) return st;
+  if (T < 0) return fail(MOE_EINVAL, "%s: T=%d is negative", fn, T);
+  if (T == 0) return MOE_OK;
+  if (!y || !topk_w || !out) return fail(MOE_EINVAL, "%s: null y, topk_w or out", fn);
+  if (d->n_shared && !shared_w) return fail(MOE_EINVAL, "%s: n_shared=1 needs shared_w", fn);
+  if (norm_out && !(eps >= 0.f && isfinite(eps)))
+    return fail(MOE_EINVAL, "%s: eps must be finite and >= 0", fn);
+  return hip_status(launch_combine(y, topk_w, shared_w, T, d->K, d->n_shared, d->H, residual, out,
+                                   norm_out, eps, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+extern "C" moe_status_t moe_rmsnorm(const uint16_t* h, int32_t T, int32_t H, float eps,
+                                    uint16_t* out, void* stream) {
+  const char* fn = "moe_rmsnorm";
+  if (T < 0 || H <= 0) return fail(MOE_EINVAL, "%s: T=%d, H=%d", fn, T, H);
+  if (!(eps >= 0.f && isfinite(eps))) return fail(MOE_EINVAL, "%s: eps must be finite and >= 0", fn);
+  if (T == 0) return MOE_OK;
+  if (!h || !out) return fail(MOE_EINVAL, "%s: null pointer", fn);
+  return hip_status(launch_rmsnorm(h, T, H, eps, out, static_cast<hipStream_t>(stream)), fn);
+}

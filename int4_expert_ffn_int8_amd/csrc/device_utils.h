@@ -1,0 +1,63 @@
+// Device helpers for the gfx950 kernels (wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi on bf16 pairs (v_dot2c_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                          __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// Two int4 codes (bits [0,4) and [16,20) of w after the shift) as the bf16
+// pair (128 + c_lo, 128 + c_hi): 0x4300 is bf16 128.0 and codes 0..15 fill
+// its low mantissa bits exactly.
+__device__ __forceinline__ uint32_t codes_to_bf16x2_biased(uint32_t w, int s) {
+  return ((w >> (4 * s)) & 0x000F000Fu) | 0x43004300u;
+}
+
+// Sum over groups of `width` consecutive lanes (width a power of two <= 64);
+// every lane of a group ends with the group's sum.  The butterfly order is
+// fixed, so results are run-to-run identical.
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = width / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Geometry of a row-streaming GEMV over an input of IN columns: each lane
+// owns 32 consecutive columns (per slice); LPR lanes cover one row and a wave
+// covers RPL rows per load; inputs wider than 2048 give each lane SL slices
+// 2048 columns apart.
+template <int IN>
+struct Geo {
+  static_assert(IN % 64 == 0 && IN >= 64 && IN <= 4096, "unsupported input width");
+  static constexpr int LPR = (IN / 32) < 64 ? (IN / 32) : 64;
+  static constexpr int RPL = 64 / LPR;
+  static constexpr int SL = (IN / 32) > 64 ? (IN / 2048) : 1;
+};
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+}  // namespace moe

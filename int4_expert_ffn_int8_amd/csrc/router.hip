@@ -1,0 +1,186 @@
+// Router: int8 group-64 gate GEMV, wavefront top-K with lowest-index ties,
+// softmax weights and the sigmoid shared-expert gate.
+//
+// [P2] "SSD 专家卸载 · Prerouter 路由预测", tier table: K of E routed experts
+// per token.  [P3] "iPhone、Mac、Android、Windows 实测横评…", quality
+// section: the router gate and the shared-expert gate are 8-bit projections.
+#include "device_utils.h"
+#include "launch.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+
+// logits[t, e] = sum_i s[e, i/64] q[e, i] x[t, i] (+ bias[e]); the row after
+// the last expert is the shared-expert gate (its logit goes to sg_logit[t]).
+// grid (ceil(rows / (4 RPL)), T), block 256.
+template <int H>
+__global__ void __launch_bounds__(256) k_router_logits(const int8_t* __restrict__ q,
+                                                        const float* __restrict__ s,
+                                                        const int8_t* __restrict__ sq,
+                                                        const float* __restrict__ ss,
+                                                        const uint16_t* __restrict__ x,
+                                                        const float* __restrict__ bias, int E,
+                                                        int n_shared, float* __restrict__ logits,
+                                                        float* __restrict__ sg_logit) {
+  using G = Geo<H>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % G::LPR;
+  const int t = blockIdx.y;
+  const int row = (blockIdx.x * 4 + wave) * G::RPL + lane / G::LPR;
+  const int rows = E + n_shared;
+  const bool valid = row < rows;
+  const int8_t* qrow = (row < E) ? q + size_t(row) * H : sq;
+  const float* srow = (row < E) ? s + size_t(row) * (H / 64) : ss;
+  float acc = 0.f;
+  if (valid) {
+#pragma unroll
+    for (int c = 0; c < G::SL; ++c) {
+      const int col0 = 32 * sub + 2048 * c;
+      const uint4 w0 = *reinterpret_cast<const uint4*>(qrow + col0);
+      const uint4 w1 = *reinterpret_cast<const uint4*>(qrow + col0 + 16);
+      const uint4* xp = reinterpret_cast<const uint4*>(x + size_t(t) * H + col0);
+      uint32_t xw[16];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint4 v = xp[k];
+        xw[4 * k] = v.x; xw[4 * k + 1] = v.y; xw[4 * k + 2] = v.z; xw[4 * k + 3] = v.w;
+      }
+      const uint32_t qw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      float part = 0.f;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int col = 4 * d + b;  // column within the lane's 32
+          const float qv = float(int8_t((qw[d] >> (8 * b)) & 0xFF));
+          const uint32_t xpair = xw[col >> 1];
+          const float xv = (col & 1) ? bf16_hi(xpair) : bf16_lo(xpair);
+          part = fmaf(qv, xv, part);
+        }
+      }
+      acc = fmaf(srow[col0 / 64], part, acc);
+    }
+  }
+  acc = group_sum<G::LPR>(acc);
+  if (valid && sub == 0) {
+    if (row < E)
+      logits[size_t(t) * E + row] = acc + (bias ? bias[row] : 0.f);
+    else
+      sg_logit[t] = acc;
+  }
+}
+
+// One wave per token: K rounds of wave argmax over (logit desc, index asc),
+// then the routing weights and the shared gate.  grid ceil(T/4), block 256.
+__global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits,
+                                               const float* __restrict__ sg_logit, int T, int E,
+                                               int K, int n_shared, int norm,
+                                               int32_t* __restrict__ idx, float* __restrict__ w,
+                                               float* __restrict__ sw) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* l = logits + size_t(t) * E;
+  constexpr int MP = kMaxE / 64;
+  float v[MP];
+  uint32_t alive = 0;
+#pragma unroll
+  for (int m = 0; m < MP; ++m) {
+    const int e = lane + 64 * m;
+    v[m] = (e < E) ? l[e] : 0.f;
+    if (e < E) alive |= 1u << m;
+  }
+  float sel_v[kMaxK];
+  int sel_e[kMaxK];
+  for (int k = 0; k < K; ++k) {
+    float bv = 0.f;
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int m = 0; m < MP; ++m) {
+      if ((alive >> m) & 1) {
+        if (be == 0x7FFFFFFF || v[m] > bv) {  // ascending e within the lane
+          bv = v[m];
+          be = lane + 64 * m;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oe = __shfl_xor(be, off, 64);
+      const bool take = (oe != 0x7FFFFFFF) &&
+                        (be == 0x7FFFFFFF || ov > bv || (ov == bv && oe < be));
+      if (take) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    sel_v[k] = bv;
+    sel_e[k] = be;
+    if ((be & 63) == lane) alive &= ~(1u << (be >> 6));
+  }
+  // weights: softmax over the selection (norm) or full softmax entries
+  const float vmax = sel_v[0];
+  float denom = 0.f;
+  if (norm) {
+    for (int k = 0; k < K; ++k) denom += expf(sel_v[k] - vmax);
+  } else {
+    float part = 0.f;
+    for (int e = lane; e < E; e += 64) part += expf(l[e] - vmax);
+    denom = group_sum<64>(part);
+  }
+  if (lane < K) {
+    float mine = 0.f;
+    int mine_e = 0;
+    for (int k = 0; k < K; ++k)
+      if (k == lane) {
+        mine = sel_v[k];
+        mine_e = sel_e[k];
+      }
+    idx[size_t(t) * K + lane] = mine_e;
+    w[size_t(t) * K + lane] = expf(mine - vmax) / denom;
+  }
+  if (n_shared && lane == 0) sw[t] = sigmoid_f(sg_logit[t]);
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+template <int H>
+static hipError_t launch_router_logits_t(const int8_t* q, const float* s, const int8_t* sq,
+                                         const float* ss, const uint16_t* x, const float* bias,
+                                         int E, int n_shared, int T, float* logits,
+                                         float* sg_logit, hipStream_t st) {
+  using G = Geo<H>;
+  const int rows = E + n_shared;
+  dim3 grid((rows + 4 * G::RPL - 1) / (4 * G::RPL), T);
+  hipLaunchKernelGGL(k_router_logits<H>, grid, dim3(256), 0, st, q, s, sq, ss, x, bias, E,
+                     n_shared, logits, sg_logit);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_logits(int H, const int8_t* q, const float* s, const int8_t* sq,
+                                const float* ss, const uint16_t* x, const float* bias, int E,
+                                int n_shared, int T, float* logits, float* sg_logit,
+                                hipStream_t st) {
+#define MOE_CASE(V) \
+  case V:           \
+    return launch_router_logits_t<V>(q, s, sq, ss, x, bias, E, n_shared, T, logits, sg_logit, st);
+  switch (H) {
+    MOE_FOR_EACH_WIDTH(MOE_CASE)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MOE_CASE
+}
+
+hipError_t launch_topk(const float* logits, const float* sg_logit, int T, int E, int K,
+                       int n_shared, int norm, int32_t* idx, float* w, float* sw,
+                       hipStream_t st) {
+  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, sg_logit, T, E, K,
+                     n_shared, norm, idx, w, sw);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,162 @@
+"""CPU checks of the C ABI library: it loads, exports every symbol the header
+declares, validates arguments before touching the GPU, and packs expert
+blobs in the documented layout.  No kernel is launched."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return re.findall(r"^MOE_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, re.M)
+
+
+@pytest.fixture(scope="module")
+def B():
+    from int4_expert_ffn_int8_amd import binding
+    binding.load()
+    return binding
+
+
+def test_library_exports_every_header_symbol(B):
+    names = _header_functions()
+    assert len(names) >= 10
+    lib = B.load()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_blob_bytes_match_layout(B):
+    # 35B-shaped expert: codes 1,572,864 + scale/bias 196,608 + LoRA 245,760
+    assert B.moe_expert_blob_bytes(2048, 512, 16) == 2015232
+    assert B.moe_expert_blob_bytes(256, 128, 4) == 64512
+    assert B.moe_expert_blob_bytes(2000, 512, 16) == 0
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(H=2000), 1), (dict(K=0), 1), (dict(K=300), 1), (dict(r=40), 2), (dict(E=2000), 2),
+    (dict(n_shared=2), 1), (dict(norm_topk=3), 1), (dict(H=8192), 2),
+])
+def test_route_rejects_bad_dims_without_launch(B, bad, code):
+    p = dict(H=2048, I=512, E=256, K=4, r=16, n_shared=1, norm_topk=1)
+    p.update(bad)
+    d = B.MoeDims(p["H"], p["I"], p["E"], p["K"], p["r"], p["n_shared"], p["norm_topk"], 1.0)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route(d, None, None, None, None, None, 1, None, None, None, None, None, None, None,
+                    None, None, stream=0)
+    assert ei.value.status == code, str(ei.value)
+
+
+def test_route_null_pointers_and_workspace(B):
+    d = B.dims(2048, 512, 256, 4, 16, 1)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route(d, None, None, None, None, None, 1, None, None, None, None, None, None, None,
+                    None, None, stream=0)
+    assert ei.value.status == 1
+    # fake non-null addresses: the workspace check fires before any launch
+    fake = 1 << 40
+    with pytest.raises(B.MoeError) as ei:
+        B.load().moe_route(B.ctypes.byref(d), fake, fake, fake, fake, fake, 1, None, fake, fake,
+                           fake, None, None, None, None, fake, 16, 0)
+        B._check(1)
+    assert "workspace" in str(ei.value)
+    # partial grouping outputs are rejected
+    st = B.load().moe_route(B.ctypes.byref(d), fake, fake, fake, fake, fake, 1, None, fake, fake,
+                            fake, None, fake, None, None, fake, 1 << 30, 0)
+    assert st == 1
+    # T == 0 is a no-op
+    assert B.load().moe_route(B.ctypes.byref(d), None, None, None, None, None, 0, None, None,
+                              None, None, None, None, None, None, None, 0, 0) == 0
+
+
+def test_expert_forward_validation(B):
+    d = B.dims(2048, 512, 256, 4, 16, 1)
+    fake = 1 << 40
+    few = B.experts_struct(fake, 64)  # no table but only 64 slots
+    st = B.load().moe_expert_forward(B.ctypes.byref(d), B.ctypes.byref(few), fake, fake, 1, fake,
+                                     None, None, None, fake, fake, 1 << 30, 0)
+    assert st == 1 and b"cover" in B.load().moe_last_error()
+    tab = B.experts_struct(fake, 64, expert_to_slot=fake)  # table but no host copy
+    st = B.load().moe_expert_forward(B.ctypes.byref(d), B.ctypes.byref(tab), fake, fake, 1, fake,
+                                     None, None, None, fake, fake, 1 << 30, 0)
+    assert st == 1 and b"host_blobs" in B.load().moe_last_error()
+    full = B.experts_struct(fake, 256)
+    st = B.load().moe_expert_forward(B.ctypes.byref(d), B.ctypes.byref(full), None, fake, 1, fake,
+                                     None, None, None, fake, fake, 1 << 30, 0)
+    assert st == 1 and b"shared_blob" in B.load().moe_last_error()
+
+
+def test_prerouter_validation(B):
+    fake = 1 << 40
+    assert B.load().prerouter_predict(fake, fake, 2048, 256, 256, 0, fake, 1, fake, None, fake,
+                                      1 << 20, 0) == 1
+    assert B.load().prerouter_predict(fake, fake, 2048, 100, 256, 4, fake, 1, fake, None, fake,
+                                      1 << 20, 0) == 1
+    assert B.load().prerouter_predict(fake, fake, 2048, 256, 256, 4, fake, 1, fake, None, fake,
+                                      16, 0) == 4
+
+
+def _unpack_codes(rows_bytes, n):
+    """Decode packed code rows with the documented nibble order:
+    word w holds columns 8w+2s in bits [4s,4s+4) and 8w+2s+1 in [16+4s, 20+4s)."""
+    words = rows_bytes.view(np.uint32)
+    out = np.zeros((words.shape[0], n), np.uint8)
+    for s in range(4):
+        out[:, 2 * s::8] = (words >> (4 * s)) & 0xF
+        out[:, 2 * s + 1::8] = (words >> (16 + 4 * s)) & 0xF
+    return out
+
+
+def test_pack_expert_layout_round_trip(B):
+    w = synth.workload(0)
+    H, I, r = w["H"], w["I"], w["r"]
+    ex = synth.expert_tensors(w, 0, 3)
+    blob = np.zeros(B.moe_expert_blob_bytes(H, I, r), np.uint8)
+    B.moe_pack_expert(H, I, r, ex, blob)
+
+    def a256(v):
+        return (v + 255) // 256 * 256
+    o = 0
+    sec = {}
+    for name, size in [("gu_codes", 2 * I * H // 2), ("gu_sb", 2 * I * (H // 64) * 4),
+                       ("dn_codes", H * I // 2), ("dn_sb", H * (I // 64) * 4),
+                       ("a_gu", 2 * r * H * 2), ("b_gu", 2 * I * r * 2), ("a_dn", r * I * 2),
+                       ("b_dn", H * r * 2)]:
+        sec[name] = blob[o:o + size]
+        o = a256(o + size)
+    assert o == blob.size
+    gu = _unpack_codes(sec["gu_codes"].reshape(2 * I, H // 2), H)
+    gu_sb = sec["gu_sb"].view(np.uint32).reshape(2 * I, H // 64)
+    b_gu = sec["b_gu"].view(np.uint16).reshape(2 * I, r)
+    for j in range(I):
+        rg = (j // 16) * 32 + j % 16
+        ru = rg + 16
+        assert np.array_equal(gu[rg], ex["q_gate"][j]) and np.array_equal(gu[ru], ex["q_up"][j])
+        assert np.array_equal(gu_sb[rg] & 0xFFFF, ex["s_gate"][j])
+        assert np.array_equal(gu_sb[rg] >> 16, ex["b_gate"][j])
+        assert np.array_equal(gu_sb[ru] & 0xFFFF, ex["s_up"][j])
+        assert np.array_equal(b_gu[rg], ex["B_gate"][j]) and np.array_equal(b_gu[ru], ex["B_up"][j])
+    dn = _unpack_codes(sec["dn_codes"].reshape(H, I // 2), I)
+    assert np.array_equal(dn, ex["q_down"])
+    dn_sb = sec["dn_sb"].view(np.uint32).reshape(H, I // 64)
+    assert np.array_equal(dn_sb >> 16, ex["b_down"])
+    a_gu = sec["a_gu"].view(np.uint16).reshape(2, r, H)
+    assert np.array_equal(a_gu[0], ex["A_gate"]) and np.array_equal(a_gu[1], ex["A_up"])
+    assert np.array_equal(sec["a_dn"].view(np.uint16).reshape(r, I), ex["A_down"])
+    assert np.array_equal(sec["b_dn"].view(np.uint16).reshape(H, r), ex["B_down"])
+
+
+def test_pack_rejects_codes_above_15(B):
+    w = synth.workload(0)
+    ex = synth.expert_tensors(w, 0, 0)
+    ex["q_down"] = ex["q_down"].copy()
+    ex["q_down"][5, 7] = 16
+    blob = np.zeros(B.moe_expert_blob_bytes(w["H"], w["I"], w["r"]), np.uint8)
+    with pytest.raises(B.MoeError):
+        B.moe_pack_expert(w["H"], w["I"], w["r"], ex, blob)
