@@ -33,7 +33,7 @@
  *     failure (thread-local).  Device faults surface at the caller's next
  *     synchronisation.  No C++ exception crosses this ABI.
  *   - Shapes supported by the kernels: H and I in {64, 128, 256, 512, 1024,
- *     2048, 4096}, 1 <= K <= E <= 1024, K <= 16, 0 <= r <= 32, n_shared in
+ *     2048, 4096}, 1 <= K <= E <= 1024, K <= 16, 0 <= r <= 16, n_shared in
  *     {0, 1}; the shared expert has the same shape (H, I, r) as the routed
  *     ones.
  */

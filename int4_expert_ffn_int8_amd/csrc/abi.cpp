@@ -4,6 +4,7 @@
 
 #include "launch.h"
 #include "moe_internal.h"
+#include "prefill.h"
 #include "status.h"
 #include "workspace.h"
 
@@ -68,18 +69,43 @@ extern "C" moe_status_t moe_route(const moe_dims_t* d, const int8_t* gate_q, con
   const WsLayout W = ws_layout(*d, T, group);
   if (!ws || ws_bytes < W.total)
     return fail(MOE_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, W.total);
-  if (group) return fail(MOE_EUNSUPPORTED, "%s: prefill grouping not built yet", fn);
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   float* lg = logits ? logits : reinterpret_cast<float*>(wsb + W.logits);
   float* sg = reinterpret_cast<float*>(wsb + W.sg);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = hip_status(launch_router_logits(d->H, gate_q, gate_s, sgate_q, sgate_s, x, logit_bias, d->E,
-                                       d->n_shared, T, lg, sg, s),
-                  fn);
+  if (T >= kRouterGemmMinT) {
+    // many tokens: MFMA GEMM over int8 codes (exact in bf16), fp32 group
+    // scale applied per 64-column chunk
+    GemmArgs g = {};
+    g.T = T;
+    g.K = d->K;
+    g.S = d->n_shared;
+    g.E = d->E;
+    g.H = d->H;
+    g.I = d->I;
+    g.x = x;
+    g.rq = gate_q;
+    g.rs = gate_s;
+    g.sq = sgate_q;
+    g.ss = sgate_s;
+    g.bias = logit_bias;
+    g.logits = lg;
+    g.sg_logit = sg;
+    st = hip_status(launch_router_gemm(g, s), fn);
+  } else {
+    st = hip_status(launch_router_logits(d->H, gate_q, gate_s, sgate_q, sgate_s, x, logit_bias,
+                                         d->E, d->n_shared, T, lg, sg, s),
+                    fn);
+  }
   if (st != MOE_OK) return st;
-  return hip_status(
+  st = hip_status(
       launch_topk(lg, sg, T, d->E, d->K, d->n_shared, d->norm_topk, topk_idx, topk_w, shared_w, s),
       fn);
+  if (st != MOE_OK || !group) return st;
+  return hip_status(launch_group(topk_idx, T, d->K, d->E, counts, offsets, perm,
+                                 reinterpret_cast<int32_t*>(wsb + W.chunk_hist),
+                                 reinterpret_cast<int32_t*>(wsb + W.base), s),
+                    fn);
 }
 
 extern "C" moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_experts_t* routed,
@@ -108,8 +134,40 @@ extern "C" moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_expert
   const WsLayout W = ws_layout(*d, T, group);
   if (!ws || ws_bytes < W.total)
     return fail(MOE_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, W.total);
-  if (group) return fail(MOE_EUNSUPPORTED, "%s: prefill path not built yet", fn);
   uint8_t* wsb = static_cast<uint8_t*>(ws);
+  const BlobLayout L = blob_layout(d->H, d->I, d->r);
+  ExpertSource src;
+  src.slots = static_cast<const uint8_t*>(routed->slots);
+  src.expert_to_slot = routed->expert_to_slot;
+  src.host_blobs = static_cast<const uint8_t*>(routed->host_blobs);
+  src.counters = routed->counters;
+  src.stride = L.total;
+  if (group) {
+    GemmArgs g = {};
+    g.T = T;
+    g.K = d->K;
+    g.S = d->n_shared;
+    g.E = d->E;
+    g.H = d->H;
+    g.I = d->I;
+    g.r = d->r;
+    g.lam = d->lora_scale;
+    g.perm = perm;
+    g.offsets = offsets;
+    g.gstart = reinterpret_cast<const int32_t*>(wsb + W.gstart);
+    g.tstart = reinterpret_cast<const int32_t*>(wsb + W.tstart);
+    g.gblob = reinterpret_cast<const unsigned long long*>(wsb + W.gblob);
+    g.L = L;
+    g.x = x;
+    g.hs = g.hs_out = reinterpret_cast<uint16_t*>(wsb + W.phs);
+    g.u = g.u_out = reinterpret_cast<uint16_t*>(wsb + W.pu);
+    g.ud = g.ud_out = reinterpret_cast<uint16_t*>(wsb + W.pud);
+    g.y = y;
+    return hip_status(launch_prefill_experts(g, counts, src,
+                                             static_cast<const uint8_t*>(shared_blob),
+                                             static_cast<hipStream_t>(stream)),
+                      fn);
+  }
   DecodeArgs a;
   a.x = x;
   a.topk_idx = topk_idx;
@@ -120,12 +178,8 @@ extern "C" moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_expert
   a.S = d->n_shared;
   a.r = d->r;
   a.lam = d->lora_scale;
-  a.L = blob_layout(d->H, d->I, d->r);
-  a.src.slots = static_cast<const uint8_t*>(routed->slots);
-  a.src.expert_to_slot = routed->expert_to_slot;
-  a.src.host_blobs = static_cast<const uint8_t*>(routed->host_blobs);
-  a.src.counters = routed->counters;
-  a.src.stride = a.L.total;
+  a.L = L;
+  a.src = src;
   a.shared_blob = static_cast<const uint8_t*>(shared_blob);
   a.blobptr = reinterpret_cast<unsigned long long*>(wsb + W.blobptr);
   a.u = reinterpret_cast<float*>(wsb + W.u);

@@ -11,13 +11,17 @@
 // the shared expert -- three kernels run:
 //   k_lora_a_decode   resolve the expert's blob through the pool table, and
 //                     u = [A_gate; A_up] x  (2r dot products over H)
-//   k_gateup_decode   a_g, a_u rows (+ lambda B u), h = silu(a_g) * a_u (bf16),
+//   k_gateup_decode   a_g, a_u rows (+ lambda B u), h = silu(a_g) * a_u (fp16),
 //                     and per-workgroup partials of v = A_down h
 //   k_down_decode     y = deq(Q_down) h + lambda B_down v
 // Each lane owns 32 consecutive input columns: one 16-byte load of int4 codes
-// per row, dequantised in registers as bf16 pairs (128 + code) and reduced
-// with v_dot2c_f32_bf16; the +128 offset is removed per half-group with the
-// lane's sum of x.  No floating-point atomics: every sum has a fixed order.
+// per row, turned in registers into exact (128 + code) pairs -- bf16 against
+// the bf16 token x, fp16 against the fp16 hidden h -- and reduced with
+// v_dot2c_f32_{bf16,f16}; the +128 offset and the affine map are applied per
+// half-group in fp32 with the lane's sum of the input.  h is kept in fp16
+// (11-bit significand): with bf16 the down projection's partial cancellation
+// turns the rounding of h into errors near 1% of the output's RMS.  No
+// floating-point atomics: every sum has a fixed order.
 #include "device_utils.h"
 #include "launch.h"
 #include "moe_internal.h"
@@ -57,9 +61,9 @@ __device__ __forceinline__ const uint8_t* resolve_blob(const DecodeArgs& a, int 
                    : a.src.host_blobs + size_t(e) * a.src.stride;
 }
 
-// Load the lane's 32-column slices of a bf16 vector as 16 bf16 pairs each,
-// plus their sums.
-template <int IN>
+// Load the lane's 32-column slices of a bf16 (or fp16) vector as 16 pairs
+// each, plus their sums.
+template <int IN, bool F16 = false>
 __device__ __forceinline__ void load_vec_slices(const uint16_t* v, int sub,
                                                 uint32_t (&xw)[Geo<IN>::SL][16],
                                                 float (&xs)[Geo<IN>::SL]) {
@@ -73,12 +77,15 @@ __device__ __forceinline__ void load_vec_slices(const uint16_t* v, int sub,
       xw[c][4 * k] = q.x; xw[c][4 * k + 1] = q.y; xw[c][4 * k + 2] = q.z; xw[c][4 * k + 3] = q.w;
     }
 #pragma unroll
-    for (int k = 0; k < 16; ++k) sum += bf16_lo(xw[c][k]) + bf16_hi(xw[c][k]);
+    for (int k = 0; k < 16; ++k)
+      sum += F16 ? f16_lo(xw[c][k]) + f16_hi(xw[c][k]) : bf16_lo(xw[c][k]) + bf16_hi(xw[c][k]);
     xs[c] = sum;
   }
 }
 
-// sum over the lane's 32 columns of (s*q + b) * x for one row slice
+// sum over the lane's 32 columns of (s*q + b) * x for one row slice; x holds
+// bf16 pairs (F16 = false) or fp16 pairs (F16 = true)
+template <bool F16 = false>
 __device__ __forceinline__ float int4_slice_dot(const uint4 q, uint32_t sbw, const uint32_t* xw,
                                                 float xs) {
   const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
@@ -86,7 +93,9 @@ __device__ __forceinline__ float int4_slice_dot(const uint4 q, uint32_t sbw, con
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = dot2_bf16(codes_to_bf16x2_biased(qw[d], s), xw[4 * d + s], acc);
+    for (int s = 0; s < 4; ++s)
+      acc = F16 ? dot2_f16(codes_to_f16x2_biased(qw[d], s), xw[4 * d + s], acc)
+                : dot2_bf16(codes_to_bf16x2_biased(qw[d], s), xw[4 * d + s], acc);
   const float sc = bf16_lo(sbw), bi = bf16_hi(sbw);
   return fmaf(sc, acc, (bi - 128.0f * sc) * xs);
 }
@@ -137,7 +146,7 @@ __global__ void __launch_bounds__(256) k_lora_a_decode(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// gate/up rows, SwiGLU, h (bf16) and partials of A_down h.
+// gate/up rows, SwiGLU, h (fp16) and partials of A_down h.
 // grid (NP, I / JW), block 256.
 template <int H>
 __global__ void __launch_bounds__(256) k_gateup_decode(DecodeArgs a) {
@@ -193,9 +202,9 @@ __global__ void __launch_bounds__(256) k_gateup_decode(DecodeArgs a) {
   if (tid < U::JW) {
     const int w = tid / U::JPW, jl = tid % U::JPW;
     const float hv = silu_f(lds_a[w][2 * jl]) * lds_a[w][2 * jl + 1];
-    const uint16_t hb = f32_to_bf16(hv);
+    const uint16_t hb = f32_to_f16_sat(hv);
     a.h[size_t(p) * a.I + blk * U::JW + tid] = hb;
-    lds_h[tid] = bf16_to_f32(hb);
+    lds_h[tid] = f16_to_f32(hb);
   }
   __syncthreads();
   if (r == 0) return;
@@ -250,7 +259,7 @@ __global__ void __launch_bounds__(256) k_down_decode(DecodeArgs a, int NB) {
   }
   uint32_t xw[G::SL][16];
   float xs[G::SL];
-  load_vec_slices<I>(a.h + size_t(p) * I, sub, xw, xs);
+  load_vec_slices<I, true>(a.h + size_t(p) * I, sub, xw, xs);
   __syncthreads();
   const uint16_t* Bd = reinterpret_cast<const uint16_t*>(blob + a.L.b_dn);
 #pragma unroll
@@ -258,7 +267,7 @@ __global__ void __launch_bounds__(256) k_down_decode(DecodeArgs a, int NB) {
     const int row = row0 + i * G::RPL + lane / G::LPR;
     float part = 0.f;
 #pragma unroll
-    for (int c = 0; c < G::SL; ++c) part += int4_slice_dot(q[i][c], sbw[i][c], xw[c], xs[c]);
+    for (int c = 0; c < G::SL; ++c) part += int4_slice_dot<true>(q[i][c], sbw[i][c], xw[c], xs[c]);
     if (row < H)
       for (int rr = sub; rr < r; rr += G::LPR)
         part = fmaf(a.lam * bf16_to_f32(Bd[size_t(row) * r + rr]), vs[rr], part);

@@ -7,6 +7,7 @@
 namespace moe {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -22,6 +23,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// fp16 <-> fp32
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return float(__builtin_bit_cast(f16x2_t, w)[0]);
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return float(__builtin_bit_cast(f16x2_t, w)[1]);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t b) {
+  return float(__builtin_bit_cast(_Float16, b));
+}
+// float -> fp16 bits, round to nearest even, saturated to the finite range
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
+  f = fminf(fmaxf(f, -65504.0f), 65504.0f);
+  return __builtin_bit_cast(uint16_t, _Float16(f));
+}
+// bf16 pair -> fp16 pair (exact for normal-range fp16 values)
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  f16x2_t v = {_Float16(bf16_lo(w)), _Float16(bf16_hi(w))};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi on fp16 pairs (v_dot2c_f32_f16)
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                acc, false);
+}
+
 // acc + a.lo*b.lo + a.hi*b.hi on bf16 pairs (v_dot2c_f32_bf16)
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -33,6 +61,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 // its low mantissa bits exactly.
 __device__ __forceinline__ uint32_t codes_to_bf16x2_biased(uint32_t w, int s) {
   return ((w >> (4 * s)) & 0x000F000Fu) | 0x43004300u;
+}
+
+// The same two codes as the fp16 pair (128 + c_lo, 128 + c_hi): 0x5800 is
+// fp16 128.0, whose mantissa step is 1/8, so each code moves to bits [3, 7).
+__device__ __forceinline__ uint32_t codes_to_f16x2_biased(uint32_t w, int s) {
+  const uint32_t t = (s == 0) ? (w << 3) : (w >> (4 * s - 3));
+  return (t & 0x00780078u) | 0x58005800u;
 }
 
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64);

@@ -10,7 +10,7 @@ namespace moe {
 constexpr int kGroup = 64;   // quantisation group along the input dimension
 constexpr int kMaxK = 16;    // experts per token supported by the top-K kernel
 constexpr int kMaxE = 1024;  // routed experts supported
-constexpr int kMaxR = 32;    // LoRA rank supported
+constexpr int kMaxR = 16;    // LoRA rank supported
 constexpr int kLoraK = 64;   // width of the LoRA chunk appended to a GEMM's K
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }

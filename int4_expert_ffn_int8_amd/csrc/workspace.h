@@ -4,6 +4,7 @@
 #include "../../include/moe.h"
 #include "launch.h"
 #include "moe_internal.h"
+#include "prefill.h"
 
 namespace moe {
 
@@ -14,13 +15,21 @@ struct WsLayout {
   // decode expert path
   size_t blobptr;  // u64 [NP]    resolved blob address per (token, slot)
   size_t u;        // fp32 [NP, 2r]
-  size_t h;        // bf16 [NP, I]
+  size_t h;        // fp16 [NP, I]
   size_t vpart;    // fp32 [NP, I/JW, r]
+  // prefill grouping and grouped GEMMs (NR = T*K + n_shared*T sorted rows)
+  size_t chunk_hist;  // int32 [nch, E]
+  size_t base;        // int32 [nch, E]
+  size_t gstart;      // int32 [E+2]
+  size_t tstart;      // int32 [E+2]
+  size_t gblob;       // u64 [E+1]
+  size_t pu;          // bf16 [NR, 64]  lambda * LoRA-A of gate/up
+  size_t pud;         // fp16 [NR, 64]  lambda * LoRA-A of down (hi/lo pairs)
+  size_t phs;         // fp16 [NR, I]   h in sorted rows
   size_t total;
 };
 
 inline WsLayout ws_layout(const moe_dims_t& d, int T, bool prefill) {
-  (void)prefill;
   WsLayout W;
   const size_t NP = size_t(T) * (d.K + d.n_shared);
   const int jw = decode_gateup_block_j(d.H);
@@ -32,6 +41,18 @@ inline WsLayout ws_layout(const moe_dims_t& d, int T, bool prefill) {
   W.u = o;       o = align256(o + NP * 2 * d.r * 4);
   W.h = o;       o = align256(o + NP * d.I * 2);
   W.vpart = o;   o = align256(o + NP * nb * d.r * 4);
+  const size_t TK = size_t(T) * d.K;
+  const size_t nch = prefill ? (TK + kGroupChunk - 1) / kGroupChunk : 0;
+  const size_t NR = prefill ? TK + size_t(d.n_shared) * T : 0;
+  const size_t E = prefill ? d.E : 0;
+  W.chunk_hist = o; o = align256(o + nch * E * 4);
+  W.base = o;       o = align256(o + nch * E * 4);
+  W.gstart = o;     o = align256(o + (prefill ? (E + 2) * 4 : 0));
+  W.tstart = o;     o = align256(o + (prefill ? (E + 2) * 4 : 0));
+  W.gblob = o;      o = align256(o + (prefill ? (E + 1) * 8 : 0));
+  W.pu = o;         o = align256(o + NR * kLoraK * 2);
+  W.pud = o;        o = align256(o + NR * kLoraK * 2);
+  W.phs = o;        o = align256(o + NR * d.I * 2);
   W.total = o;
   return W;
 }

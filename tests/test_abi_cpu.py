@@ -40,7 +40,7 @@ def test_blob_bytes_match_layout(B):
 
 
 @pytest.mark.parametrize("bad,code", [
-    (dict(H=2000), 1), (dict(K=0), 1), (dict(K=300), 1), (dict(r=40), 2), (dict(E=2000), 2),
+    (dict(H=2000), 1), (dict(K=0), 1), (dict(K=300), 1), (dict(r=17), 2), (dict(E=2000), 2),
     (dict(n_shared=2), 1), (dict(norm_topk=3), 1), (dict(H=8192), 2),
 ])
 def test_route_rejects_bad_dims_without_launch(B, bad, code):
