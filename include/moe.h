@@ -201,6 +201,41 @@ MOE_API moe_status_t moe_rmsnorm(const uint16_t* h, int32_t T, int32_t H, float 
                          void* stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_block_decode: the whole block for a few decode tokens in ONE kernel
+ * launch -- router, top-K, every selected expert and the shared expert with
+ * their LoRA deltas, the weighted combine -- with the same arithmetic as
+ * moe_route + moe_expert_forward + moe_combine.  [P2] decode paragraph: decode
+ * is the latency-critical path (route, fetch the chosen experts, compute).
+ *   flags  MOE_DECODE_NORM_INPUT: x = bf16(RMSNorm(h_in)) (unit gain, eps),
+ *          else x = h_in;  MOE_DECODE_RESIDUAL: out = bf16(h_in + block(x)),
+ *          else out = bf16(block(x)).
+ *   h_in   device bf16 [T, H];  out device bf16 [T, H] (must not alias h_in).
+ *   topk_idx int32 [T, K], topk_w fp32 [T, K]: optional copies of the
+ *          routing (NULL to skip).
+ *   ws     moe_block_decode_workspace_bytes(d, T) bytes, zeroed once with
+ *          moe_workspace_init before the first call (the library then keeps
+ *          its control words consistent from call to call).  Calls sharing a
+ *          workspace must be ordered (same stream); concurrent calls need
+ *          separate workspaces.
+ *   Supported: T <= 4 and T * (K + n_shared) <= 8; H in {256, ..., 2048},
+ *   I in {128, ..., 2048}; r <= H / 32 and r <= I / 32.  A wait that exceeds its bound (~0.2 s) sets the
+ *   sticky int32 at byte MOE_DECODE_ERR_OFFSET of ws to 1 and the call
+ *   completes with undefined output. */
+#define MOE_DECODE_NORM_INPUT 1
+#define MOE_DECODE_RESIDUAL 2
+#define MOE_DECODE_SYNC_BYTES 768
+#define MOE_DECODE_ERR_OFFSET 512
+MOE_API size_t moe_block_decode_workspace_bytes(const moe_dims_t* d, int32_t T);
+/* Zero a fused-decode workspace (a kernel, so it can be captured in a graph). */
+MOE_API moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+MOE_API moe_status_t moe_block_decode(const moe_dims_t* d, const int8_t* gate_q,
+                                      const float* gate_s, const int8_t* sgate_q,
+                                      const float* sgate_s, const moe_experts_t* routed,
+                                      const void* shared_blob, const uint16_t* h_in, int32_t T,
+                                      int32_t flags, float eps, int32_t* topk_idx, float* topk_w,
+                                      uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * prerouter_predict: the Prerouter head.  [P1] Prerouter paragraph and [P2]
  * double-shift paragraph: a light MLP after layer N predicts layer N+1's
  * top-K (for the next token) so expert loads can start early.

@@ -52,6 +52,11 @@ _SIGS = {
     "moe_combine": (c_i32, [ctypes.POINTER(MoeDims), c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp,
                             c_f32, c_vp]),
     "moe_rmsnorm": (c_i32, [c_vp, c_i32, c_i32, c_f32, c_vp, c_vp]),
+    "moe_block_decode_workspace_bytes": (c_sz, [ctypes.POINTER(MoeDims), c_i32]),
+    "moe_workspace_init": (c_i32, [c_vp, c_sz, c_vp]),
+    "moe_block_decode": (c_i32, [ctypes.POINTER(MoeDims), c_vp, c_vp, c_vp, c_vp,
+                                 ctypes.POINTER(MoeExperts), c_vp, c_vp, c_i32, c_i32, c_f32,
+                                 c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "prerouter_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32]),
     "prerouter_predict": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp,
                                   c_vp, c_vp, c_sz, c_vp]),
@@ -61,8 +66,13 @@ _SIGS = {
 HEADER_SYMBOLS = [
     "moe_last_error", "moe_expert_blob_bytes", "moe_pack_expert", "moe_workspace_bytes",
     "moe_route", "moe_expert_forward", "moe_combine", "moe_rmsnorm",
+    "moe_block_decode_workspace_bytes", "moe_workspace_init", "moe_block_decode",
     "prerouter_workspace_bytes", "prerouter_predict",
 ]
+
+DECODE_NORM_INPUT = 1
+DECODE_RESIDUAL = 2
+DECODE_ERR_OFFSET = 512  # MOE_DECODE_ERR_OFFSET
 
 
 def load(path: str = LIB_PATH):
@@ -177,3 +187,22 @@ def prerouter_predict(W1, W2, H, D, E, K, h, T, pred_idx, pred_logits, ws, strea
                                     ptr(pred_logits), ptr(ws),
                                     ws.numel() * ws.element_size() if ws is not None else 0,
                                     stream_ptr(stream)))
+
+
+def moe_block_decode_workspace_bytes(d: MoeDims, T: int) -> int:
+    return int(load().moe_block_decode_workspace_bytes(ctypes.byref(d), T))
+
+
+def moe_workspace_init(ws, stream=None) -> None:
+    _check(load().moe_workspace_init(ptr(ws), ws.numel() * ws.element_size(),
+                                     stream_ptr(stream)))
+
+
+def moe_block_decode(d, gate_q, gate_s, sgate_q, sgate_s, routed: MoeExperts, shared_blob, h_in,
+                     T, flags, eps, topk_idx, topk_w, out, ws, stream=None) -> None:
+    _check(load().moe_block_decode(ctypes.byref(d), ptr(gate_q), ptr(gate_s), ptr(sgate_q),
+                                   ptr(sgate_s), ctypes.byref(routed), ptr(shared_blob),
+                                   ptr(h_in), T, flags, eps, ptr(topk_idx), ptr(topk_w),
+                                   ptr(out), ptr(ws),
+                                   ws.numel() * ws.element_size() if ws is not None else 0,
+                                   stream_ptr(stream)))

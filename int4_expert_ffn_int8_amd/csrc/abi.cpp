@@ -4,6 +4,7 @@
 
 #include "launch.h"
 #include "moe_internal.h"
+#include "fused.h"
 #include "prefill.h"
 #include "status.h"
 #include "workspace.h"
@@ -214,4 +215,96 @@ extern "C" moe_status_t moe_rmsnorm(const uint16_t* h, int32_t T, int32_t H, flo
   if (T == 0) return MOE_OK;
   if (!h || !out) return fail(MOE_EINVAL, "%s: null pointer", fn);
   return hip_status(launch_rmsnorm(h, T, H, eps, out, static_cast<hipStream_t>(stream)), fn);
+}
+
+// ---------------------------------------------------------------------------
+// fused single-launch decode block
+// ---------------------------------------------------------------------------
+extern "C" size_t moe_block_decode_workspace_bytes(const moe_dims_t* d, int32_t T) {
+  if (check_dims(d, "moe_block_decode_workspace_bytes") != MOE_OK || T < 0) return 0;
+  return fused_ws_layout(T, d->E, d->K, d->n_shared, d->I, d->r).total;
+}
+
+extern "C" moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_workspace_init";
+  if (!ws || ws_bytes < kSyncBytes || ws_bytes % 4)
+    return fail(MOE_EINVAL, "%s: workspace must hold at least %zu bytes (a multiple of 4)", fn,
+                kSyncBytes);
+  return hip_status(launch_zero_ints(static_cast<int*>(ws), int(ws_bytes / 4),
+                                     static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+extern "C" moe_status_t moe_block_decode(const moe_dims_t* d, const int8_t* gate_q,
+                                         const float* gate_s, const int8_t* sgate_q,
+                                         const float* sgate_s, const moe_experts_t* routed,
+                                         const void* shared_blob, const uint16_t* h_in, int32_t T,
+                                         int32_t flags, float eps, int32_t* topk_idx,
+                                         float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  const char* fn = "moe_block_decode";
+  moe_status_t st = check_dims(d, fn);
+  if (st != MOE_OK) return st;
+  if (T < 0) return fail(MOE_EINVAL, "%s: T=%d is negative", fn, T);
+  if (flags & ~(MOE_DECODE_NORM_INPUT | MOE_DECODE_RESIDUAL))
+    return fail(MOE_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+  if (!fused_shape_supported(d->H, d->I, d->r))
+    return fail(MOE_EUNSUPPORTED,
+                "%s: H=%d, I=%d, r=%d (H in 256..2048, I in 128..2048, r <= H/32 and I/32)", fn,
+                d->H, d->I, d->r);
+  if (T > kFusedMaxT || T * (d->K + d->n_shared) > kFusedMaxP)
+    return fail(MOE_EUNSUPPORTED, "%s: T=%d with K+shared=%d exceeds %d tokens / %d pairs", fn,
+                T, d->K + d->n_shared, kFusedMaxT, kFusedMaxP);
+  if (!routed || !routed->slots) return fail(MOE_EINVAL, "%s: routed experts missing", fn);
+  if (routed->expert_to_slot == nullptr && routed->n_slots < d->E)
+    return fail(MOE_EINVAL, "%s: without a slot table n_slots=%d must cover E=%d experts", fn,
+                routed->n_slots, d->E);
+  if (routed->expert_to_slot != nullptr && routed->host_blobs == nullptr)
+    return fail(MOE_EINVAL, "%s: a slot table needs host_blobs for non-resident experts", fn);
+  if (d->n_shared && (!shared_blob || !sgate_q || !sgate_s))
+    return fail(MOE_EINVAL, "%s: n_shared=1 needs shared_blob, sgate_q and sgate_s", fn);
+  if ((flags & MOE_DECODE_NORM_INPUT) && !(eps >= 0.f && isfinite(eps)))
+    return fail(MOE_EINVAL, "%s: eps must be finite and >= 0", fn);
+  if (T == 0) return MOE_OK;
+  if (!gate_q || !gate_s || !h_in || !out) return fail(MOE_EINVAL, "%s: null pointer", fn);
+  const FusedWs W = fused_ws_layout(T, d->E, d->K, d->n_shared, d->I, d->r);
+  if (!ws || ws_bytes < W.total)
+    return fail(MOE_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, W.total);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  FusedArgs a = {};
+  a.T = T;
+  a.E = d->E;
+  a.K = d->K;
+  a.S = d->n_shared;
+  a.r = d->r;
+  a.H = d->H;
+  a.I = d->I;
+  a.norm_topk = d->norm_topk;
+  a.lam = d->lora_scale;
+  a.eps = eps;
+  a.norm_input = (flags & MOE_DECODE_NORM_INPUT) != 0;
+  a.residual = (flags & MOE_DECODE_RESIDUAL) != 0;
+  a.rq = gate_q;
+  a.rs = gate_s;
+  a.sq = sgate_q;
+  a.ss = sgate_s;
+  a.L = blob_layout(d->H, d->I, d->r);
+  a.src.slots = static_cast<const uint8_t*>(routed->slots);
+  a.src.expert_to_slot = routed->expert_to_slot;
+  a.src.host_blobs = static_cast<const uint8_t*>(routed->host_blobs);
+  a.src.counters = routed->counters;
+  a.src.stride = a.L.total;
+  a.shared_blob = static_cast<const uint8_t*>(shared_blob);
+  a.h_in = h_in;
+  a.out = out;
+  a.user_idx = topk_idx;
+  a.user_w = topk_w;
+  a.sync = reinterpret_cast<int*>(wsb + W.sync);
+  a.logits = reinterpret_cast<tword_t*>(wsb + W.logits);
+  a.route = reinterpret_cast<tword_t*>(wsb + W.route);
+  a.wts = reinterpret_cast<tword_t*>(wsb + W.wts);
+  a.u = reinterpret_cast<tword_t*>(wsb + W.u);
+  a.h = reinterpret_cast<tword_t*>(wsb + W.h);
+  a.vpart = reinterpret_cast<tword_t*>(wsb + W.vpart);
+  return hip_status(launch_fused(a, static_cast<hipStream_t>(stream)), fn);
 }

@@ -1,0 +1,676 @@
+// Fused decode: one launch runs a whole MoE block for a few tokens.
+//
+// [P2] "SSD 专家卸载 · Prerouter 路由预测", decode paragraph: route, then
+// stream the chosen experts, then compute.  On MI355X a decode block moves
+// ~10 MB, which HBM delivers in ~1.3 us, while each kernel boundary costs
+// several microseconds; so the block is one kernel whose workgroups take
+// roles and hand results to each other through device memory:
+//
+//   router    logits of its gate rows (x = optional RMSNorm of h_in, done
+//             redundantly and identically in every workgroup); the last
+//             router workgroup also waits for every logit and runs the
+//             wavefront top-K, publishing ids, weights and the shared gate.
+//   lora_a    u = [A_gate; A_up] x for one (token, slot) pair.
+//   gate_up   32 gate/up outputs of one pair (+ lambda B u), SwiGLU -> h
+//             (fp16), and that block's partial of v = A_down h.
+//   down      a block of output rows for every pair: v = sum of the pair's
+//             partials (fixed order), y = deq(Q_down) h + lambda B_down v,
+//             then the weighted combine (+ residual) -> out.
+//
+// Weight loads are issued before the waits they do not depend on (shared
+// expert from the start, routed experts as soon as their ids arrive).  A role
+// waits only on roles with lower workgroup ids, which the dispatcher starts
+// first, and every wait is bounded: on timeout the kernel records an error
+// and still runs to completion.
+//
+// Hand-off protocol.  The 8 XCDs have separate L2 caches, and a device-scope
+// release/acquire fence writes back / invalidates a whole L2, which at one
+// fence per workgroup costs far more than the block itself.  So every value
+// one workgroup hands to another is a 64-bit word -- payload in the low half,
+// the launch's tag in the high half -- written and read with device-scope
+// relaxed atomics (sc1 stores and loads that the XCD L2s do not hold
+// incoherently).  A producer just stores; a consumer polls one word (from one
+// thread, with sleeps, so waiting costs little bandwidth), then loads every
+// word it needs and repeats the loads until all of them carry this launch's
+// tag.  The tag is the launch epoch + 1; the last workgroup to finish bumps
+// the epoch, so stale words of earlier launches never match and nothing needs
+// clearing.  Weights and inputs, read-only in the kernel, use ordinary cached
+// loads.
+#include "device_utils.h"
+#include "fused.h"
+#include "launch.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int add_dev(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int* slot(const FusedArgs& a, int s) { return a.sync + s * kSlotInts; }
+
+// this launch's tag (epoch + 1, never 0)
+__device__ __forceinline__ unsigned launch_tag(const FusedArgs& a) {
+  return (unsigned(ld_dev(slot(a, kSlotEpoch))) % 0x7FFFFFFFu) + 1u;
+}
+__device__ __forceinline__ tword_t tw(unsigned tag, uint32_t bits) {
+  return (tword_t(tag) << 32) | bits;
+}
+__device__ __forceinline__ tword_t twf(unsigned tag, float v) { return tw(tag, __float_as_uint(v)); }
+__device__ __forceinline__ bool has_tag(tword_t w, unsigned tag) { return unsigned(w >> 32) == tag; }
+__device__ __forceinline__ float wf(tword_t w) { return __uint_as_float(uint32_t(w)); }
+
+__device__ __forceinline__ void set_err(const FusedArgs& a) { st_dev(slot(a, kSlotErr), 1); }
+
+// one thread waits (bounded, with sleeps) until *w carries `tag`
+__device__ __forceinline__ tword_t poll_word(const FusedArgs& a, const tword_t* w, unsigned tag) {
+  unsigned n = 0;
+  tword_t v;
+  while (!has_tag(v = ld_dev(w), tag)) {
+    __builtin_amdgcn_s_sleep(20);
+    if (++n > kFusedSpinLimit) {
+      set_err(a);
+      break;
+    }
+  }
+  return v;
+}
+
+// Workgroup-wide retry of a load round: true once every thread's words were
+// valid; sleeps between rounds and gives up (recording the error) after the
+// spin limit.
+__device__ __forceinline__ bool round_done(const FusedArgs& a, bool ok, unsigned& n) {
+  if (__syncthreads_and(ok)) return true;
+  if (++n > kFusedSpinLimit) {
+    if (threadIdx.x == 0) set_err(a);
+    return true;
+  }
+  __builtin_amdgcn_s_sleep(20);
+  return false;
+}
+
+// pair index of work unit q: shared-expert pairs first (they need no routing)
+__device__ __forceinline__ int pair_of_unit(const FusedArgs& a, int q) {
+  const int KS = a.K + a.S;
+  if (q < a.S * a.T) return q * KS + a.K;
+  q -= a.S * a.T;
+  return (q / a.K) * KS + q % a.K;
+}
+
+// blob of routed expert e (pool lookup)
+__device__ __forceinline__ const uint8_t* expert_blob(const FusedArgs& a, int e, bool count) {
+  if (a.src.expert_to_slot == nullptr) return a.src.slots + size_t(e) * a.src.stride;
+  const int s = a.src.expert_to_slot[e];
+  if (count && a.src.counters) {
+    atomicAdd(&a.src.counters[1], 1ull);
+    if (s >= 0) atomicAdd(&a.src.counters[0], 1ull);
+  }
+  return s >= 0 ? a.src.slots + size_t(s) * a.src.stride : a.src.host_blobs + size_t(e) * a.src.stride;
+}
+
+// Expert id of routed pair p, published by the top-K (workgroup-uniform).
+__device__ __forceinline__ int wait_expert(const FusedArgs& a, int p, unsigned tag, int* lds_int) {
+  const int KS = a.K + a.S;
+  if (threadIdx.x == 0)
+    *lds_int = int(uint32_t(poll_word(a, &a.route[(p / KS) * a.K + p % KS], tag)));
+  __syncthreads();
+  return *lds_int;
+}
+
+// The lane's 32 columns of the token input x (bf16 pairs) and their sum.
+// With norm, x = bf16(h * rsqrt(mean(h^2) + eps)); the lanes of one row group
+// cover all H columns, so the mean needs no cross-wave step and every
+// workgroup computes bit-identical x.
+template <int H>
+__device__ __forceinline__ void token_slice(const FusedArgs& a, int t, int sub, uint32_t (&xw)[16],
+                                            float& xs) {
+  using G = Geo<H>;
+  const uint4* hp = reinterpret_cast<const uint4*>(a.h_in + size_t(t) * H + 32 * sub);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint4 v = hp[k];
+    xw[4 * k] = v.x; xw[4 * k + 1] = v.y; xw[4 * k + 2] = v.z; xw[4 * k + 3] = v.w;
+  }
+  if (a.norm_input) {
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float lo = bf16_lo(xw[k]), hi = bf16_hi(xw[k]);
+      ss = fmaf(lo, lo, ss);
+      ss = fmaf(hi, hi, ss);
+    }
+    ss = group_sum<G::LPR>(ss);
+    const float inv = 1.0f / sqrtf(ss / float(H) + a.eps);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) xw[k] = pack_bf16x2(bf16_lo(xw[k]) * inv, bf16_hi(xw[k]) * inv);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) s += bf16_lo(xw[k]) + bf16_hi(xw[k]);
+  xs = s;
+}
+
+// (s*q + b) . v over the lane's 32 columns; v is bf16 (F16 false) or fp16
+template <bool F16>
+__device__ __forceinline__ float slice_dot(const uint4 q, uint32_t sbw, const uint32_t* xw,
+                                           float xs) {
+  const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = F16 ? dot2_f16(codes_to_f16x2_biased(qw[d], s), xw[4 * d + s], acc)
+                : dot2_bf16(codes_to_bf16x2_biased(qw[d], s), xw[4 * d + s], acc);
+  const float sc = bf16_lo(sbw), bi = bf16_hi(sbw);
+  return fmaf(sc, acc, (bi - 128.0f * sc) * xs);
+}
+
+// ---------------------------------------------------------------------------
+template <int H>
+__device__ void role_router(const FusedArgs& a, int b) {
+  using G = Geo<H>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane % G::LPR;
+  const int row = (b * 4 + wave) * G::RPL + lane / G::LPR;
+  const int rows = a.E + a.S;
+  const bool valid = row < rows;
+  uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
+  float sc = 0.f;
+  if (valid) {
+    const int8_t* q = (row < a.E) ? a.rq + size_t(row) * H : a.sq;
+    const float* s = (row < a.E) ? a.rs + size_t(row) * (H / 64) : a.ss;
+    w0 = *reinterpret_cast<const uint4*>(q + 32 * sub);
+    w1 = *reinterpret_cast<const uint4*>(q + 32 * sub + 16);
+    sc = s[sub >> 1];
+  }
+  const unsigned tag = launch_tag(a);
+  const uint32_t qw[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  for (int t = 0; t < a.T; ++t) {
+    uint32_t xw[16];
+    float xs;
+    token_slice<H>(a, t, sub, xw, xs);
+    float part = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int col = 4 * d + bb;
+        const float qv = float(int8_t((qw[d] >> (8 * bb)) & 0xFF));
+        part = fmaf(qv, (col & 1) ? bf16_hi(xw[col >> 1]) : bf16_lo(xw[col >> 1]), part);
+      }
+    part = group_sum<G::LPR>(sc * part);
+    // column E of the logits row holds the shared-gate logit
+    if (valid && sub == 0) st_dev(&a.logits[t * (a.E + 1) + row], twf(tag, part));
+  }
+  if (b != a.nR - 1) return;
+  // The last router workgroup: wait for every logit of its token (one wave
+  // per token), then K rounds of wave argmax by (logit desc, index asc).
+  for (int t = wave; t < a.T; t += 4) {
+    const tword_t* l = a.logits + t * (a.E + 1);
+    constexpr int MP = kMaxE / 64;
+    float v[MP];
+    uint32_t alive = 0;
+    float sgl = 0.f;
+    for (unsigned n = 0;; ++n) {
+      bool ok = true;
+#pragma unroll
+      for (int m = 0; m < MP; ++m) {
+        const int e = lane + 64 * m;
+        if (e < a.E) {
+          const tword_t w = ld_dev(&l[e]);
+          ok = ok && has_tag(w, tag);
+          v[m] = wf(w);
+        }
+      }
+      if (a.S && lane == 0) {
+        const tword_t w = ld_dev(&l[a.E]);
+        ok = ok && has_tag(w, tag);
+        sgl = wf(w);
+      }
+      if (__all(ok)) break;
+      if (++n > kFusedSpinLimit) {
+        if (lane == 0) set_err(a);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(20);
+    }
+#pragma unroll
+    for (int m = 0; m < MP; ++m)
+      if (lane + 64 * m < a.E) alive |= 1u << m;
+    float first = 0.f, denom = 0.f, mine = 0.f;
+    int mine_e = 0;
+    for (int k = 0; k < a.K; ++k) {
+      float bv = 0.f;
+      int be = 0x7FFFFFFF;
+#pragma unroll
+      for (int m = 0; m < MP; ++m)
+        if (((alive >> m) & 1) && (be == 0x7FFFFFFF || v[m] > bv)) {
+          bv = v[m];
+          be = lane + 64 * m;
+        }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oe = __shfl_xor(be, off, 64);
+        if (oe != 0x7FFFFFFF && (be == 0x7FFFFFFF || ov > bv || (ov == bv && oe < be))) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      if ((be & 63) == lane) alive &= ~(1u << (be >> 6));
+      if (k == 0) first = bv;
+      const float ev = expf(bv - first);
+      denom += ev;
+      if (k == lane) {
+        mine = ev;
+        mine_e = be;
+      }
+    }
+    if (!a.norm_topk) {  // full-softmax entries: denominator over all E
+      float part = 0.f;
+#pragma unroll
+      for (int m = 0; m < MP; ++m)
+        if (lane + 64 * m < a.E) part += expf(v[m] - first);
+      denom = group_sum<64>(part);
+    }
+    if (lane < a.K) {
+      const float wv = mine / denom;
+      st_dev(&a.route[t * a.K + lane], tw(tag, uint32_t(mine_e)));
+      st_dev(&a.wts[t * (a.K + 1) + lane], twf(tag, wv));
+      if (a.user_idx) a.user_idx[t * a.K + lane] = mine_e;
+      if (a.user_w) a.user_w[t * a.K + lane] = wv;
+    }
+    if (a.S && lane == 0) st_dev(&a.wts[t * (a.K + 1) + a.K], twf(tag, sigmoid_f(sgl)));
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int H>
+__device__ void role_lora_a(const FusedArgs& a, int unit, int part, int* lds_int) {
+  using G = Geo<H>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane % G::LPR;
+  const int p = pair_of_unit(a, unit);
+  const int KS = a.K + a.S;
+  const int t = p / KS;
+  const bool routed = (p % KS) < a.K;
+  const unsigned tag = launch_tag(a);
+  uint32_t xw[16];
+  float xs;
+  token_slice<H>(a, t, sub, xw, xs);
+  const uint8_t* blob = a.shared_blob;
+  if (routed) blob = expert_blob(a, wait_expert(a, p, tag, lds_int), false);
+  const uint16_t* A = reinterpret_cast<const uint16_t*>(blob + a.L.a_gu);
+  const int rows = 2 * a.r;
+  const int row0 = part * 8 * G::RPL;  // 4 waves x 2 loads x RPL rows
+  float acc[2] = {0.f, 0.f};
+  int rw[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    rw[i] = row0 + (2 * wave + i) * G::RPL + lane / G::LPR;
+    if (rw[i] < rows) {
+      const uint4* ap = reinterpret_cast<const uint4*>(A + size_t(rw[i]) * H + 32 * sub);
+      uint4 q[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) q[k] = ap[k];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[i] = dot2_bf16(q[k].x, xw[4 * k], acc[i]);
+        acc[i] = dot2_bf16(q[k].y, xw[4 * k + 1], acc[i]);
+        acc[i] = dot2_bf16(q[k].z, xw[4 * k + 2], acc[i]);
+        acc[i] = dot2_bf16(q[k].w, xw[4 * k + 3], acc[i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float v = group_sum<G::LPR>(acc[i]);
+    if (rw[i] < rows && sub == 0) st_dev(&a.u[p * rows + rw[i]], twf(tag, v));
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int H>
+__device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, int* lds_int) {
+  using G = Geo<H>;
+  constexpr int RPL = G::RPL;
+  constexpr int JW = kFusedJW, JPW = JW / 4;  // outputs per workgroup / wave
+  constexpr int NR = 2 * JPW, NL = NR / RPL;  // gate + up rows per wave, loads per lane
+  static_assert(NR % RPL == 0, "rows per wave");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane % G::LPR;
+  const int tid = threadIdx.x;
+  const int p = pair_of_unit(a, unit);
+  const int KS = a.K + a.S;
+  const int t = p / KS;
+  const bool routed = (p % KS) < a.K;
+  const int j0 = blk * JW + wave * JPW;
+  const int r = a.r;
+  const unsigned tag = launch_tag(a);
+  const uint8_t* blob = a.shared_blob;
+  if (routed) blob = expert_blob(a, wait_expert(a, p, tag, lds_int), false);
+  // every weight this workgroup needs, before anything waits on data
+  const uint8_t* codes = blob + a.L.gu_codes;
+  const uint32_t* sb = reinterpret_cast<const uint32_t*>(blob + a.L.gu_sb);
+  const uint16_t* Bgu = reinterpret_cast<const uint16_t*>(blob + a.L.b_gu);
+  const uint16_t* Ad = reinterpret_cast<const uint16_t*>(blob + a.L.a_dn);
+  uint4 q[NL];
+  uint32_t sbw[NL];
+  int brow[NL];
+  float bl[NL];  // lambda * B[row][sub] (one LoRA rank per lane; r <= LPR)
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int ri = i * RPL + lane / G::LPR;
+    const int j = j0 + (ri >> 1);
+    brow[i] = (ri & 1) ? gu_row_up(j) : gu_row_gate(j);
+    q[i] = *reinterpret_cast<const uint4*>(codes + size_t(brow[i]) * (H / 2) + 16 * sub);
+    sbw[i] = sb[size_t(brow[i]) * (H / 64) + (sub >> 1)];
+    bl[i] = (sub < r) ? a.lam * bf16_to_f32(Bgu[size_t(brow[i]) * r + sub]) : 0.f;
+  }
+  // A_down entries for this block's partial of v: two products per thread
+  float ad[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int id = c * 256 + tid, rr = id / JW, jj = id % JW;
+    ad[c] = (rr < r) ? bf16_to_f32(Ad[size_t(rr) * a.I + blk * JW + jj]) : 0.f;
+  }
+  uint32_t xw[16];
+  float xs;
+  token_slice<H>(a, t, sub, xw, xs);
+  float part[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) part[i] = slice_dot<false>(q[i], sbw[i], xw, xs);
+  float* lds_a = lds;           // [4][NR]
+  float* lds_h = lds + 4 * NR;  // [JW]
+  if (r > 0) {  // u = A x of this pair (from its lora_a workgroups)
+    float uv[2] = {0.f, 0.f};  // lane's rank `sub` of A_gate x and A_up x
+    if (tid == 0) poll_word(a, &a.u[p * 2 * r + 2 * r - 1], tag);
+    for (unsigned n = 0;; ++n) {
+      bool ok = true;
+      if (sub < r) {
+        const tword_t g = ld_dev(&a.u[p * 2 * r + sub]);
+        const tword_t uu = ld_dev(&a.u[p * 2 * r + r + sub]);
+        ok = has_tag(g, tag) && has_tag(uu, tag);
+        uv[0] = wf(g);
+        uv[1] = wf(uu);
+      }
+      if (round_done(a, ok, n)) break;
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int ri = i * RPL + lane / G::LPR;
+      part[i] = fmaf(bl[i], uv[ri & 1], part[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const float v = group_sum<G::LPR>(part[i]);
+    if (sub == 0) lds_a[wave * NR + i * RPL + lane / G::LPR] = v;
+  }
+  __syncthreads();
+  if (tid < JW) {
+    const int w = tid / JPW, jl = tid % JPW;
+    const float hv = silu_f(lds_a[w * NR + 2 * jl]) * lds_a[w * NR + 2 * jl + 1];
+    lds_h[tid] = f16_to_f32(f32_to_f16_sat(hv));
+  }
+  __syncthreads();
+  if (tid < JW / 2) {  // h as fp16 pairs, one tagged word per pair
+    f16x2_t pr = {_Float16(lds_h[2 * tid]), _Float16(lds_h[2 * tid + 1])};
+    st_dev(&a.h[p * (a.I / 2) + blk * (JW / 2) + tid], tw(tag, __builtin_bit_cast(uint32_t, pr)));
+  }
+  if (r > 0) {  // this block's partial of v = A_down h
+    const int NB = a.I / JW;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int id = c * 256 + tid, rr = id / JW, jj = id % JW;
+      const float prod = group_sum<JW>(ad[c] * lds_h[jj]);
+      if (jj == 0 && rr < r) st_dev(&a.vpart[(p * NB + blk) * r + rr], twf(tag, prod));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int H, int I>
+__device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* lds_v,
+                          float* lds_wt, int* lds_idx) {
+  using G = Geo<I>;
+  constexpr int RPL = G::RPL;
+  constexpr int NB = I / kFusedJW;  // partials of A_down h per pair
+  constexpr int MAXH = (kFusedMaxP * I / 2 + 255) / 256;
+  constexpr int MAXC = (kFusedMaxP * kMaxR * 16 + 255) / 256;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane % G::LPR;
+  const int tid = threadIdx.x;
+  const int row = d * 4 * RPL + wave * RPL + lane / G::LPR;
+  const bool valid = row < H;
+  const int KS = a.K + a.S;
+  const int P = a.T * KS;
+  const int r = a.r;
+  const unsigned tag = launch_tag(a);
+  // Prefetch this lane's down-row slice of every pair into registers: the
+  // shared expert at once, routed experts as soon as their ids arrive.
+  uint4 q[kFusedMaxP];
+  uint32_t sbw[kFusedMaxP];
+  float bd[kFusedMaxP];  // lambda * B_down[row][sub]
+  const uint8_t* bl[kFusedMaxP];
+  auto fetch = [&](int p) {
+    q[p] = *reinterpret_cast<const uint4*>(bl[p] + a.L.dn_codes + size_t(row) * (I / 2) + 16 * sub);
+    sbw[p] = reinterpret_cast<const uint32_t*>(bl[p] + a.L.dn_sb)[size_t(row) * (I / 64) + (sub >> 1)];
+    bd[p] = (sub < r) ? a.lam * bf16_to_f32(reinterpret_cast<const uint16_t*>(bl[p] + a.L.b_dn)
+                                                [size_t(row) * r + sub])
+                      : 0.f;
+  };
+#pragma unroll
+  for (int p = 0; p < kFusedMaxP; ++p) {
+    q[p] = make_uint4(0, 0, 0, 0);
+    sbw[p] = 0;
+    bd[p] = 0.f;
+    bl[p] = a.shared_blob;
+    if (p < P && (p % KS) >= a.K && valid) fetch(p);
+  }
+  // routed expert ids: one polling thread per pair
+  if (tid < P) {
+    const int t = tid / KS, k = tid % KS;
+    lds_idx[tid] = (k < a.K) ? int(uint32_t(poll_word(a, &a.route[t * a.K + k], tag))) : -1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < kFusedMaxP; ++p) {
+    if (p < P && (p % KS) < a.K) {
+      bl[p] = expert_blob(a, lds_idx[p], d == 0 && tid == 0);  // one count per lookup
+      if (valid) fetch(p);
+    }
+  }
+  // wait for the last h word, then load every pair's h, v partials and
+  // routing weights until all carry this launch's tag
+  if (tid == 0) poll_word(a, &a.h[P * (I / 2) - 1], tag);
+  __syncthreads();
+  tword_t hv[MAXH], vp[MAXC];
+  float wtv = 0.f;
+  for (unsigned n = 0;; ++n) {
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < MAXH; ++k) {
+      const int i = tid + 256 * k;
+      if (i < P * (I / 2)) {
+        hv[k] = ld_dev(&a.h[i]);
+        ok = ok && has_tag(hv[k], tag);
+      }
+    }
+    if (r > 0) {
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) {
+        const int id = c * 256 + tid;
+        const int pr = id >> 4, q16 = id & 15;
+        const int p = pr / r, rr = pr % r;
+        vp[c] = 0;
+        if (p < P && q16 < NB) {  // NB <= 16 here; larger NB is summed below
+          vp[c] = ld_dev(&a.vpart[(p * NB + q16) * r + rr]);
+          ok = ok && has_tag(vp[c], tag);
+        }
+      }
+    }
+    if (tid < P) {
+      const int t = tid / KS, k = tid % KS;
+      const tword_t w = ld_dev(&a.wts[t * (a.K + 1) + (k < a.K ? k : a.K)]);
+      ok = ok && has_tag(w, tag);
+      wtv = wf(w);
+    }
+    if (round_done(a, ok, n)) break;
+  }
+  // partial blocks beyond the first 16 (I > 512): summed after the round
+  float vs[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int id = c * 256 + tid;
+    const int pr = id >> 4, q16 = id & 15;
+    const int p = pr / r, rr = pr % r;
+    float s = (r > 0 && p < P && q16 < NB) ? wf(vp[c]) : 0.f;
+    if (r > 0 && p < P)
+      for (int bb = q16 + 16; bb < NB; bb += 16) {
+        const tword_t w = poll_word(a, &a.vpart[(p * NB + bb) * r + rr], tag);
+        s += wf(w);
+      }
+    vs[c] = s;
+  }
+  {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(lds_hh);
+#pragma unroll
+    for (int k = 0; k < MAXH; ++k) {
+      const int i = tid + 256 * k;
+      if (i < P * (I / 2)) dst[i] = uint32_t(hv[k]);
+    }
+  }
+  if (r > 0) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int id = c * 256 + tid;
+      const int pr = id >> 4, q16 = id & 15;
+      const int p = pr / r, rr = pr % r;
+      const float s = group_sum<16>(vs[c]);
+      if (q16 == 0 && p < P) lds_v[p * kMaxR + rr] = s;
+    }
+  }
+  if (tid < P) lds_wt[tid] = wtv;
+  __syncthreads();
+  float o[kFusedMaxT];
+#pragma unroll
+  for (int t = 0; t < kFusedMaxT; ++t) o[t] = 0.f;
+#pragma unroll
+  for (int p = 0; p < kFusedMaxP; ++p) {
+    if (p >= P) continue;
+    uint32_t hw[16];
+    const uint4* hp = reinterpret_cast<const uint4*>(lds_hh + p * I + 32 * sub);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint4 v = hp[k];
+      hw[4 * k] = v.x; hw[4 * k + 1] = v.y; hw[4 * k + 2] = v.z; hw[4 * k + 3] = v.w;
+    }
+    float hs = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) hs += f16_lo(hw[k]) + f16_hi(hw[k]);
+    float y = slice_dot<true>(q[p], sbw[p], hw, hs);
+    if (sub < r) y = fmaf(bd[p], lds_v[p * kMaxR + sub], y);
+    y = group_sum<G::LPR>(y);
+    const int t = p / KS;
+    const float wk = lds_wt[p];
+#pragma unroll
+    for (int tt = 0; tt < kFusedMaxT; ++tt)
+      if (tt == t) o[tt] = fmaf(wk, y, o[tt]);
+  }
+  if (valid && sub == 0) {
+#pragma unroll
+    for (int t = 0; t < kFusedMaxT; ++t) {
+      if (t >= a.T) break;
+      float v = o[t];
+      if (a.residual) v += bf16_to_f32(a.h_in[size_t(t) * H + row]);
+      a.out[size_t(t) * H + row] = f32_to_bf16(v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int H, int I>
+__global__ void __launch_bounds__(256) k_fused_decode(FusedArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds_hh[kFusedMaxP * I];
+  __shared__ __attribute__((aligned(16))) float lds_f[kFusedMaxP * kMaxR + 160];
+  __shared__ float lds_wt[kFusedMaxP];
+  __shared__ int lds_i[kFusedMaxP];
+  const int b = blockIdx.x;
+  if (b < a.nR) {
+    role_router<H>(a, b);
+  } else if (b < a.base_gu) {
+    const int i = b - a.base_la;
+    role_lora_a<H>(a, i / a.nWA, i % a.nWA, lds_i);
+  } else if (b < a.base_dn) {
+    const int i = b - a.base_gu;
+    role_gate_up<H>(a, i / a.nBG, i % a.nBG, lds_f, lds_i);
+  } else {
+    role_down<H, I>(a, b - a.base_dn, lds_hh, lds_f, lds_wt, lds_i);
+  }
+  // the last workgroup out starts the next epoch
+  __syncthreads();
+  if (threadIdx.x == 0 && add_dev(slot(a, kSlotDone), 1) == a.total - 1) {
+    const int e = ld_dev(slot(a, kSlotEpoch));
+    st_dev(slot(a, kSlotDone), 0);
+    st_dev(slot(a, kSlotEpoch), e + 1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int H, int I>
+static hipError_t launch_fused_t(FusedArgs a, hipStream_t st) {
+  constexpr int RPL_H = Geo<H>::RPL;
+  const int P = a.T * (a.K + a.S);
+  a.nR = (a.E + a.S + 4 * RPL_H - 1) / (4 * RPL_H);
+  a.nWA = a.r > 0 ? (2 * a.r + 8 * RPL_H - 1) / (8 * RPL_H) : 0;
+  a.nBG = a.I / kFusedJW;
+  a.nD = (H + 4 * Geo<I>::RPL - 1) / (4 * Geo<I>::RPL);
+  a.base_la = a.nR;
+  a.base_gu = a.base_la + P * a.nWA;
+  a.base_dn = a.base_gu + P * a.nBG;
+  a.total = a.base_dn + a.nD;
+  hipLaunchKernelGGL((k_fused_decode<H, I>), dim3(a.total), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+bool fused_shape_supported(int H, int I, int r) {
+  // one LoRA rank per lane of a row group: r <= H / 32 and r <= I / 32
+  return (H == 256 || H == 512 || H == 1024 || H == 2048) &&
+         (I == 128 || I == 256 || I == 512 || I == 1024 || I == 2048) && r <= H / 32 &&
+         r <= I / 32;
+}
+
+hipError_t launch_fused(const FusedArgs& a, hipStream_t st) {
+#define MOE_CASE_I(HV, IV) \
+  case IV:                 \
+    return launch_fused_t<HV, IV>(a, st);
+#define MOE_CASE_H(HV)                                                                        \
+  case HV:                                                                                    \
+    switch (a.I) {                                                                            \
+      MOE_CASE_I(HV, 128) MOE_CASE_I(HV, 256) MOE_CASE_I(HV, 512) MOE_CASE_I(HV, 1024)        \
+      MOE_CASE_I(HV, 2048) default : return hipErrorInvalidValue;                             \
+    }
+  switch (a.H) {
+    MOE_CASE_H(256) MOE_CASE_H(512) MOE_CASE_H(1024) MOE_CASE_H(2048)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MOE_CASE_H
+#undef MOE_CASE_I
+}
+
+__global__ void k_zero_ints(int* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+hipError_t launch_zero_ints(int* p, int n, hipStream_t st) {
+  hipLaunchKernelGGL(k_zero_ints, dim3(1), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

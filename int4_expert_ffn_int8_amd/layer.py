@@ -10,12 +10,34 @@ import torch
 from . import binding as B
 
 
-def pack_experts(H: int, I: int, r: int, experts) -> np.ndarray:
-    """Pack logical expert tensors (dicts of numpy arrays) into blobs [n, bytes]."""
+def pack_experts(H: int, I: int, r: int, experts, n: int | None = None, threads: int = 1,
+                 out: np.ndarray | None = None) -> np.ndarray:
+    """Pack logical expert tensors into blobs [n, bytes].
+
+    `experts` is a list of dicts of numpy arrays, or a callable e -> dict
+    (then `n` experts are produced and packed on `threads` threads; the
+    packer releases the GIL).  `out` may be a preallocated (e.g. pinned)
+    uint8 array of shape [n, blob_bytes]."""
     nb = B.moe_expert_blob_bytes(H, I, r)
-    out = np.zeros((len(experts), nb), np.uint8)
-    for i, ex in enumerate(experts):
-        B.moe_pack_expert(H, I, r, ex, out[i])
+    if callable(experts):
+        make = experts
+    else:
+        lst = list(experts)
+        n = len(lst)
+        make = lst.__getitem__
+    if out is None:
+        out = np.zeros((n, nb), np.uint8)
+
+    def one(i):
+        B.moe_pack_expert(H, I, r, make(i), out[i])
+
+    if threads <= 1:
+        for i in range(n):
+            one(i)
+    else:
+        import concurrent.futures
+        with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, range(n)))
     return out
 
 
@@ -89,3 +111,31 @@ class MoeLayer:
         self.experts_forward(x, b, routed, stream)
         self.combine(b, residual, norm_out, eps, stream)
         return b["out"]
+
+    # ---- fused single-launch decode -----------------------------------
+    def fused_buffers(self, T: int) -> dict:
+        dv = self.device
+        ws = torch.empty((B.moe_block_decode_workspace_bytes(self.d, T),),
+                         dtype=torch.uint8, device=dv)
+        B.moe_workspace_init(ws)
+        return {
+            "T": T,
+            "ws": ws,
+            "idx": torch.empty((T, self.K), dtype=torch.int32, device=dv),
+            "w": torch.empty((T, self.K), dtype=torch.float32, device=dv),
+            "out": torch.empty((T, self.H), dtype=torch.int16, device=dv),
+        }
+
+    def decode_fused(self, h_in, fb, flags=0, eps=1e-6, out=None, routed=None, stream=None):
+        """One kernel launch: route + experts + combine (+ norm / residual)."""
+        out = fb["out"] if out is None else out
+        B.moe_block_decode(self.d, self.gate_q, self.gate_s, self.sgate_q, self.sgate_s,
+                           routed or self.experts, self.shared_blob, h_in, fb["T"], flags, eps,
+                           fb["idx"], fb["w"], out, fb["ws"], stream)
+        return out
+
+    @staticmethod
+    def fused_error_word(fb) -> int:
+        """Sticky timeout flag of the fused kernel (0 = every wait completed)."""
+        o = B.DECODE_ERR_OFFSET
+        return int(fb["ws"][o:o + 4].view(torch.int32).item())

@@ -3,7 +3,8 @@
 Recipe (the pages print no weights, so every value is drawn here):
 
 * routed and shared expert projections gate/up/down: uint4 codes uniform in
-  {0..15} (one code per element, uint8 array), per-64-column-group scale
+  {0..15} (one code per element, uint8 array; each random byte supplies two
+  independent codes, low nibble first), per-64-column-group scale
   |N(0, 0.02)| and bias N(0, 0.01), both rounded to bf16;
 * LoRA factors A [r, in] and B [out, r]: N(0, 0.02) rounded to bf16;
 * router gate and shared-expert gate: int8 codes uniform in [-127, 127] with a
@@ -68,8 +69,10 @@ def _rng(seed: int, wid: int, layer: int, tensor: str, index: int = 0):
 def f32_to_bf16_bits(a) -> np.ndarray:
     """Round float32 values to bf16 (nearest, ties to even); uint16 bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = a.view(np.uint32)
+    # finite floats have bit patterns below 0xFF800000, so u + 0x8000 cannot
+    # wrap in 32 bits (values are drawn finite)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return r.astype(np.uint16)
 
 
@@ -78,6 +81,15 @@ def _bf16_normal(rng, std, shape, absval=False):
     if absval:
         v = np.abs(v)
     return f32_to_bf16_bits(v)
+
+
+def _codes(rng, shape) -> np.ndarray:
+    n = int(np.prod(shape))
+    b = np.frombuffer(rng.bytes((n + 1) // 2), dtype=np.uint8)
+    c = np.empty(2 * b.size, dtype=np.uint8)
+    c[0::2] = b & 15
+    c[1::2] = b >> 4
+    return c[:n].reshape(shape)
 
 
 def expert_tensors(w: dict, layer: int, expert: int, seed: int = 0) -> dict:
@@ -93,8 +105,7 @@ def expert_tensors(w: dict, layer: int, expert: int, seed: int = 0) -> dict:
     out = {}
     for p in _PROJ:
         o, i = shapes[p]
-        out[f"q_{p}"] = _rng(seed, wid, layer, f"q_{p}", expert).integers(
-            0, 16, size=(o, i), dtype=np.uint8)
+        out[f"q_{p}"] = _codes(_rng(seed, wid, layer, f"q_{p}", expert), (o, i))
         out[f"s_{p}"] = _bf16_normal(_rng(seed, wid, layer, f"s_{p}", expert),
                                      0.02, (o, i // 64), absval=True)
         out[f"b_{p}"] = _bf16_normal(_rng(seed, wid, layer, f"b_{p}", expert),
