@@ -70,14 +70,70 @@ __device__ __forceinline__ uint32_t codes_to_f16x2_biased(uint32_t w, int s) {
   return (t & 0x00780078u) | 0x58005800u;
 }
 
+// Cross-lane moves without LDS round trips (gfx9 DPP).  Row permutations
+// (quad_perm [1,0,3,2] / [2,3,0,1], row_half_mirror, row_mirror) exchange
+// within 16-lane rows; row_bcast:15 adds lane 15 of rows 0 and 2 into rows 1
+// and 3, row_bcast:31 adds lane 31 into rows 2 and 3 (other rows get the
+// `old` operand, 0 here).
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within 8
+constexpr int kDppMirror = 0x140;      // lane i <- 15 - i within 16
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v, uint32_t old = 0) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(v), CTRL, ROWS, 0xF, false));
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_f(float v, float old = 0.f) {
+  return __uint_as_float(dpp_u<CTRL, ROWS>(__float_as_uint(v), __float_as_uint(old)));
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64);
-// every lane of a group ends with the group's sum.  The butterfly order is
-// fixed, so results are run-to-run identical.
+// every lane of a group ends with the group's sum.  The pairing is the fixed
+// butterfly (partners 1, 2, 4, 8, 16, 32 lanes apart): every lane of a group
+// holds the bit-identical sum and results are run-to-run identical.
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = width / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  if constexpr (width >= 2) v += dpp_f<kDppXor1>(v);
+  if constexpr (width >= 4) v += dpp_f<kDppXor2>(v);
+  if constexpr (width >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (width >= 16) v += dpp_f<kDppMirror>(v);
+  if constexpr (width >= 32) v += dpp_f<kDppBcast15, 0xA>(v);  // lanes 31, 63: 32-lane sums
+  if constexpr (width == 32) {
+    const float lo = readlane_f(v, 31), hi = readlane_f(v, 63);
+    v = (__lane_id() < 32) ? lo : hi;
+  }
+  if constexpr (width == 64) {
+    v += dpp_f<kDppBcast31, 0xC>(v);  // lane 63: the wave sum
+    v = readlane_f(v, 63);
+  }
   return v;
+}
+
+// Wave-wide max / min; the result is wave-uniform.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  v = fmaxf(v, dpp_f<kDppBcast15, 0xA>(v, v));
+  v = fmaxf(v, dpp_f<kDppBcast31, 0xC>(v, v));
+  return readlane_f(v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u<kDppXor1>(v));
+  v = min(v, dpp_u<kDppXor2>(v));
+  v = min(v, dpp_u<kDppHalfMirror>(v));
+  v = min(v, dpp_u<kDppMirror>(v));
+  v = min(v, dpp_u<kDppBcast15, 0xA>(v, v));
+  v = min(v, dpp_u<kDppBcast31, 0xC>(v, v));
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
 }
 
 // Geometry of a row-streaming GEMV over an input of IN columns: each lane

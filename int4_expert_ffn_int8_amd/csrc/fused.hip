@@ -36,6 +36,12 @@
 // the epoch, so stale words of earlier launches never match and nothing needs
 // clearing.  Weights and inputs, read-only in the kernel, use ordinary cached
 // loads.
+//
+// Load discipline.  Vector loads complete in order, so a load whose value is
+// used inside a divergent branch makes the wave wait for every load issued
+// before it.  Every batch of loads here is therefore issued unconditionally
+// (indices clamped to valid elements), and guards, tag checks and arithmetic
+// run in a second pass.
 #include "device_utils.h"
 #include "fused.h"
 #include "launch.h"
@@ -74,7 +80,7 @@ __device__ __forceinline__ tword_t poll_word(const FusedArgs& a, const tword_t* 
   unsigned n = 0;
   tword_t v;
   while (!has_tag(v = ld_dev(w), tag)) {
-    __builtin_amdgcn_s_sleep(20);
+    __builtin_amdgcn_s_sleep(2);
     if (++n > kFusedSpinLimit) {
       set_err(a);
       break;
@@ -92,7 +98,7 @@ __device__ __forceinline__ bool round_done(const FusedArgs& a, bool ok, unsigned
     if (threadIdx.x == 0) set_err(a);
     return true;
   }
-  __builtin_amdgcn_s_sleep(20);
+  __builtin_amdgcn_s_sleep(2);
   return false;
 }
 
@@ -219,27 +225,23 @@ __device__ void role_router(const FusedArgs& a, int b) {
     uint32_t alive = 0;
     float sgl = 0.f;
     for (unsigned n = 0;; ++n) {
-      bool ok = true;
+      tword_t w[MP];
+#pragma unroll
+      for (int m = 0; m < MP; ++m) w[m] = ld_dev(&l[min(lane + 64 * m, a.E - 1)]);
+      const tword_t ws = ld_dev(&l[a.E]);  // shared-gate logit (unused without S)
+      unsigned bad = unsigned(a.S != 0) & unsigned(!has_tag(ws, tag));
 #pragma unroll
       for (int m = 0; m < MP; ++m) {
-        const int e = lane + 64 * m;
-        if (e < a.E) {
-          const tword_t w = ld_dev(&l[e]);
-          ok = ok && has_tag(w, tag);
-          v[m] = wf(w);
-        }
+        bad |= unsigned(lane + 64 * m < a.E) & unsigned(!has_tag(w[m], tag));
+        v[m] = wf(w[m]);
       }
-      if (a.S && lane == 0) {
-        const tword_t w = ld_dev(&l[a.E]);
-        ok = ok && has_tag(w, tag);
-        sgl = wf(w);
-      }
-      if (__all(ok)) break;
+      sgl = wf(ws);
+      if (__all(bad == 0)) break;
       if (++n > kFusedSpinLimit) {
         if (lane == 0) set_err(a);
         break;
       }
-      __builtin_amdgcn_s_sleep(20);
+      __builtin_amdgcn_s_sleep(2);
     }
 #pragma unroll
     for (int m = 0; m < MP; ++m)
@@ -247,30 +249,26 @@ __device__ void role_router(const FusedArgs& a, int b) {
     float first = 0.f, denom = 0.f, mine = 0.f;
     int mine_e = 0;
     for (int k = 0; k < a.K; ++k) {
-      float bv = 0.f;
-      int be = 0x7FFFFFFF;
+      // lane-local best (lowest index among equal logits), then the wave max
+      // and the lowest index that holds it
+      constexpr uint32_t kNone = 0xFFFFFFFFu;
+      float bv = -INFINITY;
+      uint32_t be = kNone;
 #pragma unroll
       for (int m = 0; m < MP; ++m)
-        if (((alive >> m) & 1) && (be == 0x7FFFFFFF || v[m] > bv)) {
+        if (((alive >> m) & 1) && (be == kNone || v[m] > bv)) {
           bv = v[m];
           be = lane + 64 * m;
         }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oe = __shfl_xor(be, off, 64);
-        if (oe != 0x7FFFFFFF && (be == 0x7FFFFFFF || ov > bv || (ov == bv && oe < be))) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if ((be & 63) == lane) alive &= ~(1u << (be >> 6));
-      if (k == 0) first = bv;
-      const float ev = expf(bv - first);
+      const float mx = wave_max(bv);
+      const uint32_t sel = wave_min_u32((be != kNone && bv == mx) ? be : kNone);
+      if ((sel & 63) == uint32_t(lane)) alive &= ~(1u << (sel >> 6));
+      if (k == 0) first = mx;
+      const float ev = expf(mx - first);
       denom += ev;
       if (k == lane) {
         mine = ev;
-        mine_e = be;
+        mine_e = int(sel);
       }
     }
     if (!a.norm_topk) {  // full-softmax entries: denominator over all E
@@ -311,23 +309,23 @@ __device__ void role_lora_a(const FusedArgs& a, int unit, int part, int* lds_int
   const int row0 = part * 8 * G::RPL;  // 4 waves x 2 loads x RPL rows
   float acc[2] = {0.f, 0.f};
   int rw[2];
+  uint4 q[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     rw[i] = row0 + (2 * wave + i) * G::RPL + lane / G::LPR;
-    if (rw[i] < rows) {
-      const uint4* ap = reinterpret_cast<const uint4*>(A + size_t(rw[i]) * H + 32 * sub);
-      uint4 q[4];
+    const uint4* ap = reinterpret_cast<const uint4*>(A + size_t(min(rw[i], rows - 1)) * H + 32 * sub);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) q[k] = ap[k];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc[i] = dot2_bf16(q[k].x, xw[4 * k], acc[i]);
-        acc[i] = dot2_bf16(q[k].y, xw[4 * k + 1], acc[i]);
-        acc[i] = dot2_bf16(q[k].z, xw[4 * k + 2], acc[i]);
-        acc[i] = dot2_bf16(q[k].w, xw[4 * k + 3], acc[i]);
-      }
-    }
+    for (int k = 0; k < 4; ++k) q[i][k] = ap[k];
   }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[i] = dot2_bf16(q[i][k].x, xw[4 * k], acc[i]);
+      acc[i] = dot2_bf16(q[i][k].y, xw[4 * k + 1], acc[i]);
+      acc[i] = dot2_bf16(q[i][k].z, xw[4 * k + 2], acc[i]);
+      acc[i] = dot2_bf16(q[i][k].w, xw[4 * k + 3], acc[i]);
+    }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const float v = group_sum<G::LPR>(acc[i]);
@@ -362,7 +360,9 @@ __device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, 
   uint4 q[NL];
   uint32_t sbw[NL];
   int brow[NL];
-  float bl[NL];  // lambda * B[row][sub] (one LoRA rank per lane; r <= LPR)
+  uint16_t braw[NL];  // B[row][sub] (one LoRA rank per lane; r <= LPR)
+  uint16_t adraw[2];  // A_down entries of this block's partial of v
+  const int rc = max(r - 1, 0);
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int ri = i * RPL + lane / G::LPR;
@@ -370,14 +370,15 @@ __device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, 
     brow[i] = (ri & 1) ? gu_row_up(j) : gu_row_gate(j);
     q[i] = *reinterpret_cast<const uint4*>(codes + size_t(brow[i]) * (H / 2) + 16 * sub);
     sbw[i] = sb[size_t(brow[i]) * (H / 64) + (sub >> 1)];
-    bl[i] = (sub < r) ? a.lam * bf16_to_f32(Bgu[size_t(brow[i]) * r + sub]) : 0.f;
   }
-  // A_down entries for this block's partial of v: two products per thread
-  float ad[2];
+  if (r > 0) {
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int id = c * 256 + tid, rr = id / JW, jj = id % JW;
-    ad[c] = (rr < r) ? bf16_to_f32(Ad[size_t(rr) * a.I + blk * JW + jj]) : 0.f;
+    for (int i = 0; i < NL; ++i) braw[i] = Bgu[size_t(brow[i]) * r + min(sub, rc)];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int id = c * 256 + tid, rr = min(id / JW, rc), jj = id % JW;
+      adraw[c] = Ad[size_t(rr) * a.I + blk * JW + jj];
+    }
   }
   uint32_t xw[16];
   float xs;
@@ -389,28 +390,27 @@ __device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, 
   float* lds_h = lds + 4 * NR;  // [JW]
   if (r > 0) {  // u = A x of this pair (from its lora_a workgroups)
     float uv[2] = {0.f, 0.f};  // lane's rank `sub` of A_gate x and A_up x
-    if (tid == 0) poll_word(a, &a.u[p * 2 * r + 2 * r - 1], tag);
     for (unsigned n = 0;; ++n) {
-      bool ok = true;
-      if (sub < r) {
-        const tword_t g = ld_dev(&a.u[p * 2 * r + sub]);
-        const tword_t uu = ld_dev(&a.u[p * 2 * r + r + sub]);
-        ok = has_tag(g, tag) && has_tag(uu, tag);
-        uv[0] = wf(g);
-        uv[1] = wf(uu);
-      }
+      const tword_t g = ld_dev(&a.u[p * 2 * r + min(sub, rc)]);
+      const tword_t uu = ld_dev(&a.u[p * 2 * r + r + min(sub, rc)]);
+      const bool ok = has_tag(g, tag) && has_tag(uu, tag);
+      uv[0] = wf(g);
+      uv[1] = wf(uu);
       if (round_done(a, ok, n)) break;
     }
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int ri = i * RPL + lane / G::LPR;
-      part[i] = fmaf(bl[i], uv[ri & 1], part[i]);
+      const float bl = (sub < r) ? a.lam * bf16_to_f32(braw[i]) : 0.f;
+      part[i] = fmaf(bl, uv[ri & 1], part[i]);
     }
   }
+  // all sums first (independent chains interleave), then the stores
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const float v = group_sum<G::LPR>(part[i]);
-    if (sub == 0) lds_a[wave * NR + i * RPL + lane / G::LPR] = v;
+  for (int i = 0; i < NL; ++i) part[i] = group_sum<G::LPR>(part[i]);
+  if (sub == 0) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) lds_a[wave * NR + i * RPL + lane / G::LPR] = part[i];
   }
   __syncthreads();
   if (tid < JW) {
@@ -428,7 +428,8 @@ __device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, 
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int id = c * 256 + tid, rr = id / JW, jj = id % JW;
-      const float prod = group_sum<JW>(ad[c] * lds_h[jj]);
+      const float ad = (rr < r) ? bf16_to_f32(adraw[c]) : 0.f;
+      const float prod = group_sum<JW>(ad * lds_h[jj]);
       if (jj == 0 && rr < r) st_dev(&a.vpart[(p * NB + blk) * r + rr], twf(tag, prod));
     }
   }
@@ -455,23 +456,27 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
   // shared expert at once, routed experts as soon as their ids arrive.
   uint4 q[kFusedMaxP];
   uint32_t sbw[kFusedMaxP];
-  float bd[kFusedMaxP];  // lambda * B_down[row][sub]
+  uint16_t bdraw[kFusedMaxP];  // B_down[row][sub]
   const uint8_t* bl[kFusedMaxP];
-  auto fetch = [&](int p) {
-    q[p] = *reinterpret_cast<const uint4*>(bl[p] + a.L.dn_codes + size_t(row) * (I / 2) + 16 * sub);
-    sbw[p] = reinterpret_cast<const uint32_t*>(bl[p] + a.L.dn_sb)[size_t(row) * (I / 64) + (sub >> 1)];
-    bd[p] = (sub < r) ? a.lam * bf16_to_f32(reinterpret_cast<const uint16_t*>(bl[p] + a.L.b_dn)
-                                                [size_t(row) * r + sub])
-                      : 0.f;
+  const int rowc = min(row, H - 1), subr = min(sub, max(r - 1, 0));
+  auto fetch = [&](int p) {  // p is workgroup-uniform: no divergent guard
+    q[p] = *reinterpret_cast<const uint4*>(bl[p] + a.L.dn_codes + size_t(rowc) * (I / 2) + 16 * sub);
+    sbw[p] = reinterpret_cast<const uint32_t*>(bl[p] + a.L.dn_sb)[size_t(rowc) * (I / 64) + (sub >> 1)];
+    if (r > 0)
+      bdraw[p] = reinterpret_cast<const uint16_t*>(bl[p] + a.L.b_dn)[size_t(rowc) * r + subr];
   };
 #pragma unroll
   for (int p = 0; p < kFusedMaxP; ++p) {
     q[p] = make_uint4(0, 0, 0, 0);
     sbw[p] = 0;
-    bd[p] = 0.f;
+    bdraw[p] = 0;
     bl[p] = a.shared_blob;
-    if (p < P && (p % KS) >= a.K && valid) fetch(p);
+    if (p < P && (p % KS) >= a.K) fetch(p);
   }
+  float resid[kFusedMaxT];  // residual input of this lane's row, read early
+#pragma unroll
+  for (int t = 0; t < kFusedMaxT; ++t)
+    resid[t] = bf16_to_f32(a.h_in[size_t(min(t, a.T - 1)) * H + rowc]);
   // routed expert ids: one polling thread per pair
   if (tid < P) {
     const int t = tid / KS, k = tid % KS;
@@ -482,7 +487,7 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
   for (int p = 0; p < kFusedMaxP; ++p) {
     if (p < P && (p % KS) < a.K) {
       bl[p] = expert_blob(a, lds_idx[p], d == 0 && tid == 0);  // one count per lookup
-      if (valid) fetch(p);
+      fetch(p);
     }
   }
   // wait for the last h word, then load every pair's h, v partials and
@@ -491,36 +496,37 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
   __syncthreads();
   tword_t hv[MAXH], vp[MAXC];
   float wtv = 0.f;
+  const int nh = P * (I / 2);
+  const int tw_t = min(tid, P - 1) / KS, tw_k = min(tid, P - 1) % KS;
+  const int tw_i = tw_t * (a.K + 1) + (tw_k < a.K ? tw_k : a.K);
+  // partial of v read by slot c of this thread: (pair, rank, block < 16);
+  // without LoRA every slot reads a valid dummy word and is not checked
+  const tword_t* vsrc = (r > 0) ? a.vpart : a.wts;
+  int vidx[MAXC];
+  uint32_t vneed = 0;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int id = c * 256 + tid;
+    const int pr = id >> 4, q16 = id & 15;
+    const int p = (r > 0) ? pr / r : P, rr = (r > 0) ? pr % r : 0;
+    const bool need = p < P && q16 < NB;  // NB <= 16 here; larger NB is summed below
+    vidx[c] = need ? (p * NB + q16) * r + rr : 0;
+    vneed |= uint32_t(need) << c;
+  }
   for (unsigned n = 0;; ++n) {
-    bool ok = true;
+    // every load of the round first (fixed count, clamped indices), then the checks
 #pragma unroll
-    for (int k = 0; k < MAXH; ++k) {
-      const int i = tid + 256 * k;
-      if (i < P * (I / 2)) {
-        hv[k] = ld_dev(&a.h[i]);
-        ok = ok && has_tag(hv[k], tag);
-      }
-    }
-    if (r > 0) {
+    for (int k = 0; k < MAXH; ++k) hv[k] = ld_dev(&a.h[min(tid + 256 * k, nh - 1)]);
 #pragma unroll
-      for (int c = 0; c < MAXC; ++c) {
-        const int id = c * 256 + tid;
-        const int pr = id >> 4, q16 = id & 15;
-        const int p = pr / r, rr = pr % r;
-        vp[c] = 0;
-        if (p < P && q16 < NB) {  // NB <= 16 here; larger NB is summed below
-          vp[c] = ld_dev(&a.vpart[(p * NB + q16) * r + rr]);
-          ok = ok && has_tag(vp[c], tag);
-        }
-      }
-    }
-    if (tid < P) {
-      const int t = tid / KS, k = tid % KS;
-      const tword_t w = ld_dev(&a.wts[t * (a.K + 1) + (k < a.K ? k : a.K)]);
-      ok = ok && has_tag(w, tag);
-      wtv = wf(w);
-    }
-    if (round_done(a, ok, n)) break;
+    for (int c = 0; c < MAXC; ++c) vp[c] = ld_dev(&vsrc[vidx[c]]);
+    const tword_t w = ld_dev(&a.wts[tw_i]);
+    unsigned bad = unsigned(tid < P) & unsigned(!has_tag(w, tag));
+    wtv = wf(w);
+#pragma unroll
+    for (int k = 0; k < MAXH; ++k) bad |= unsigned(tid + 256 * k < nh) & unsigned(!has_tag(hv[k], tag));
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) bad |= ((vneed >> c) & 1u) & unsigned(!has_tag(vp[c], tag));
+    if (round_done(a, bad == 0, n)) break;
   }
   // partial blocks beyond the first 16 (I > 512): summed after the round
   float vs[MAXC];
@@ -528,9 +534,9 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
   for (int c = 0; c < MAXC; ++c) {
     const int id = c * 256 + tid;
     const int pr = id >> 4, q16 = id & 15;
-    const int p = pr / r, rr = pr % r;
-    float s = (r > 0 && p < P && q16 < NB) ? wf(vp[c]) : 0.f;
-    if (r > 0 && p < P)
+    const int p = (r > 0) ? pr / r : P, rr = (r > 0) ? pr % r : 0;
+    float s = ((vneed >> c) & 1u) ? wf(vp[c]) : 0.f;
+    if (p < P)
       for (int bb = q16 + 16; bb < NB; bb += 16) {
         const tword_t w = poll_word(a, &a.vpart[(p * NB + bb) * r + rr], tag);
         s += wf(w);
@@ -574,7 +580,7 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
 #pragma unroll
     for (int k = 0; k < 16; ++k) hs += f16_lo(hw[k]) + f16_hi(hw[k]);
     float y = slice_dot<true>(q[p], sbw[p], hw, hs);
-    if (sub < r) y = fmaf(bd[p], lds_v[p * kMaxR + sub], y);
+    if (sub < r) y = fmaf(a.lam * bf16_to_f32(bdraw[p]), lds_v[p * kMaxR + sub], y);
     y = group_sum<G::LPR>(y);
     const int t = p / KS;
     const float wk = lds_wt[p];
@@ -587,7 +593,7 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
     for (int t = 0; t < kFusedMaxT; ++t) {
       if (t >= a.T) break;
       float v = o[t];
-      if (a.residual) v += bf16_to_f32(a.h_in[size_t(t) * H + row]);
+      if (a.residual) v += resid[t];
       a.out[size_t(t) * H + row] = f32_to_bf16(v);
     }
   }

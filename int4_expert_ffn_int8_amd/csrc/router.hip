@@ -94,31 +94,23 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits,
   float sel_v[kMaxK];
   int sel_e[kMaxK];
   for (int k = 0; k < K; ++k) {
-    float bv = 0.f;
-    int be = 0x7FFFFFFF;
+    // lane-local best (ascending e within the lane keeps the lowest index
+    // among equal logits), then the wave max and the lowest index holding it
+    constexpr uint32_t kNone = 0xFFFFFFFFu;
+    float bv = -INFINITY;
+    uint32_t be = kNone;
 #pragma unroll
     for (int m = 0; m < MP; ++m) {
-      if ((alive >> m) & 1) {
-        if (be == 0x7FFFFFFF || v[m] > bv) {  // ascending e within the lane
-          bv = v[m];
-          be = lane + 64 * m;
-        }
+      if (((alive >> m) & 1) && (be == kNone || v[m] > bv)) {
+        bv = v[m];
+        be = lane + 64 * m;
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      const bool take = (oe != 0x7FFFFFFF) &&
-                        (be == 0x7FFFFFFF || ov > bv || (ov == bv && oe < be));
-      if (take) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    sel_v[k] = bv;
-    sel_e[k] = be;
-    if ((be & 63) == lane) alive &= ~(1u << (be >> 6));
+    const float mx = wave_max(bv);
+    const uint32_t sel = wave_min_u32((be != kNone && bv == mx) ? be : kNone);
+    sel_v[k] = mx;
+    sel_e[k] = int(sel);
+    if ((sel & 63) == uint32_t(lane)) alive &= ~(1u << (sel >> 6));
   }
   // weights: softmax over the selection (norm) or full softmax entries
   const float vmax = sel_v[0];
