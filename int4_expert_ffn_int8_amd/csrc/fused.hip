@@ -46,6 +46,7 @@
 #include "fused.h"
 #include "launch.h"
 #include "moe_internal.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -222,7 +223,6 @@ __device__ void role_router(const FusedArgs& a, int b) {
     const tword_t* l = a.logits + t * (a.E + 1);
     constexpr int MP = kMaxE / 64;
     float v[MP];
-    uint32_t alive = 0;
     float sgl = 0.f;
     for (unsigned n = 0;; ++n) {
       tword_t w[MP];
@@ -243,26 +243,9 @@ __device__ void role_router(const FusedArgs& a, int b) {
       }
       __builtin_amdgcn_s_sleep(2);
     }
-#pragma unroll
-    for (int m = 0; m < MP; ++m)
-      if (lane + 64 * m < a.E) alive |= 1u << m;
     float first = 0.f, denom = 0.f, mine = 0.f;
     int mine_e = 0;
-    for (int k = 0; k < a.K; ++k) {
-      // lane-local best (lowest index among equal logits), then the wave max
-      // and the lowest index that holds it
-      constexpr uint32_t kNone = 0xFFFFFFFFu;
-      float bv = -INFINITY;
-      uint32_t be = kNone;
-#pragma unroll
-      for (int m = 0; m < MP; ++m)
-        if (((alive >> m) & 1) && (be == kNone || v[m] > bv)) {
-          bv = v[m];
-          be = lane + 64 * m;
-        }
-      const float mx = wave_max(bv);
-      const uint32_t sel = wave_min_u32((be != kNone && bv == mx) ? be : kNone);
-      if ((sel & 63) == uint32_t(lane)) alive &= ~(1u << (sel >> 6));
+    topk_wave(v, a.E, a.K, lane, [&](int k, float mx, uint32_t sel) {
       if (k == 0) first = mx;
       const float ev = expf(mx - first);
       denom += ev;
@@ -270,7 +253,7 @@ __device__ void role_router(const FusedArgs& a, int b) {
         mine = ev;
         mine_e = int(sel);
       }
-    }
+    });
     if (!a.norm_topk) {  // full-softmax entries: denominator over all E
       float part = 0.f;
 #pragma unroll
@@ -306,31 +289,21 @@ __device__ void role_lora_a(const FusedArgs& a, int unit, int part, int* lds_int
   if (routed) blob = expert_blob(a, wait_expert(a, p, tag, lds_int), false);
   const uint16_t* A = reinterpret_cast<const uint16_t*>(blob + a.L.a_gu);
   const int rows = 2 * a.r;
-  const int row0 = part * 8 * G::RPL;  // 4 waves x 2 loads x RPL rows
-  float acc[2] = {0.f, 0.f};
-  int rw[2];
-  uint4 q[2][4];
+  const int rw = part * 4 * G::RPL + wave * G::RPL + lane / G::LPR;  // 4 waves x RPL rows
+  uint4 q[4];
+  const uint4* ap = reinterpret_cast<const uint4*>(A + size_t(min(rw, rows - 1)) * H + 32 * sub);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    rw[i] = row0 + (2 * wave + i) * G::RPL + lane / G::LPR;
-    const uint4* ap = reinterpret_cast<const uint4*>(A + size_t(min(rw[i], rows - 1)) * H + 32 * sub);
+  for (int k = 0; k < 4; ++k) q[k] = ap[k];
+  float acc = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) q[i][k] = ap[k];
+  for (int k = 0; k < 4; ++k) {
+    acc = dot2_bf16(q[k].x, xw[4 * k], acc);
+    acc = dot2_bf16(q[k].y, xw[4 * k + 1], acc);
+    acc = dot2_bf16(q[k].z, xw[4 * k + 2], acc);
+    acc = dot2_bf16(q[k].w, xw[4 * k + 3], acc);
   }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc[i] = dot2_bf16(q[i][k].x, xw[4 * k], acc[i]);
-      acc[i] = dot2_bf16(q[i][k].y, xw[4 * k + 1], acc[i]);
-      acc[i] = dot2_bf16(q[i][k].z, xw[4 * k + 2], acc[i]);
-      acc[i] = dot2_bf16(q[i][k].w, xw[4 * k + 3], acc[i]);
-    }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float v = group_sum<G::LPR>(acc[i]);
-    if (rw[i] < rows && sub == 0) st_dev(&a.u[p * rows + rw[i]], twf(tag, v));
-  }
+  acc = group_sum<G::LPR>(acc);
+  if (rw < rows && sub == 0) st_dev(&a.u[p * rows + rw], twf(tag, acc));
 }
 
 // ---------------------------------------------------------------------------
@@ -437,7 +410,7 @@ __device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, 
 
 // ---------------------------------------------------------------------------
 template <int H, int I>
-__device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* lds_v,
+__device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* lds_hs, float* lds_v,
                           float* lds_wt, int* lds_idx) {
   using G = Geo<I>;
   constexpr int RPL = G::RPL;
@@ -544,11 +517,18 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
     vs[c] = s;
   }
   {
+    // h words to LDS, and the sum of each 32-column slice (16 consecutive
+    // words, held by 16 consecutive threads) for the affine term
     uint32_t* dst = reinterpret_cast<uint32_t*>(lds_hh);
 #pragma unroll
     for (int k = 0; k < MAXH; ++k) {
       const int i = tid + 256 * k;
-      if (i < P * (I / 2)) dst[i] = uint32_t(hv[k]);
+      const uint32_t hw = uint32_t(hv[k]);
+      const float ss = group_sum<16>(f16_lo(hw) + f16_hi(hw));
+      if (i < nh) {
+        dst[i] = hw;
+        if ((i & 15) == 0) lds_hs[i >> 4] = ss;
+      }
     }
   }
   if (r > 0) {
@@ -576,10 +556,7 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
       const uint4 v = hp[k];
       hw[4 * k] = v.x; hw[4 * k + 1] = v.y; hw[4 * k + 2] = v.z; hw[4 * k + 3] = v.w;
     }
-    float hs = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) hs += f16_lo(hw[k]) + f16_hi(hw[k]);
-    float y = slice_dot<true>(q[p], sbw[p], hw, hs);
+    float y = slice_dot<true>(q[p], sbw[p], hw, lds_hs[p * (I / 32) + sub]);
     if (sub < r) y = fmaf(a.lam * bf16_to_f32(bdraw[p]), lds_v[p * kMaxR + sub], y);
     y = group_sum<G::LPR>(y);
     const int t = p / KS;
@@ -603,6 +580,7 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
 template <int H, int I>
 __global__ void __launch_bounds__(256) k_fused_decode(FusedArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_hh[kFusedMaxP * I];
+  __shared__ float lds_hs[kFusedMaxP * I / 32];
   __shared__ __attribute__((aligned(16))) float lds_f[kFusedMaxP * kMaxR + 160];
   __shared__ float lds_wt[kFusedMaxP];
   __shared__ int lds_i[kFusedMaxP];
@@ -616,7 +594,7 @@ __global__ void __launch_bounds__(256) k_fused_decode(FusedArgs a) {
     const int i = b - a.base_gu;
     role_gate_up<H>(a, i / a.nBG, i % a.nBG, lds_f, lds_i);
   } else {
-    role_down<H, I>(a, b - a.base_dn, lds_hh, lds_f, lds_wt, lds_i);
+    role_down<H, I>(a, b - a.base_dn, lds_hh, lds_hs, lds_f, lds_wt, lds_i);
   }
   // the last workgroup out starts the next epoch
   __syncthreads();
@@ -633,7 +611,7 @@ static hipError_t launch_fused_t(FusedArgs a, hipStream_t st) {
   constexpr int RPL_H = Geo<H>::RPL;
   const int P = a.T * (a.K + a.S);
   a.nR = (a.E + a.S + 4 * RPL_H - 1) / (4 * RPL_H);
-  a.nWA = a.r > 0 ? (2 * a.r + 8 * RPL_H - 1) / (8 * RPL_H) : 0;
+  a.nWA = a.r > 0 ? (2 * a.r + 4 * RPL_H - 1) / (4 * RPL_H) : 0;
   a.nBG = a.I / kFusedJW;
   a.nD = (H + 4 * Geo<I>::RPL - 1) / (4 * Geo<I>::RPL);
   a.base_la = a.nR;

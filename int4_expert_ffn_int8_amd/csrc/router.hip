@@ -7,6 +7,7 @@
 #include "device_utils.h"
 #include "launch.h"
 #include "moe_internal.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -84,54 +85,30 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits,
   const float* l = logits + size_t(t) * E;
   constexpr int MP = kMaxE / 64;
   float v[MP];
-  uint32_t alive = 0;
 #pragma unroll
-  for (int m = 0; m < MP; ++m) {
-    const int e = lane + 64 * m;
-    v[m] = (e < E) ? l[e] : 0.f;
-    if (e < E) alive |= 1u << m;
-  }
-  float sel_v[kMaxK];
-  int sel_e[kMaxK];
-  for (int k = 0; k < K; ++k) {
-    // lane-local best (ascending e within the lane keeps the lowest index
-    // among equal logits), then the wave max and the lowest index holding it
-    constexpr uint32_t kNone = 0xFFFFFFFFu;
-    float bv = -INFINITY;
-    uint32_t be = kNone;
-#pragma unroll
-    for (int m = 0; m < MP; ++m) {
-      if (((alive >> m) & 1) && (be == kNone || v[m] > bv)) {
-        bv = v[m];
-        be = lane + 64 * m;
-      }
+  for (int m = 0; m < MP; ++m) v[m] = l[min(lane + 64 * m, E - 1)];  // entries >= E are not read
+  // softmax weights over the selection (norm) or full-softmax entries
+  float first = 0.f, denom = 0.f, mine = 0.f;
+  int mine_e = 0;
+  topk_wave(v, E, K, lane, [&](int k, float mx, uint32_t sel) {
+    if (k == 0) first = mx;
+    const float ev = expf(mx - first);
+    denom += ev;
+    if (k == lane) {
+      mine = ev;
+      mine_e = int(sel);
     }
-    const float mx = wave_max(bv);
-    const uint32_t sel = wave_min_u32((be != kNone && bv == mx) ? be : kNone);
-    sel_v[k] = mx;
-    sel_e[k] = int(sel);
-    if ((sel & 63) == uint32_t(lane)) alive &= ~(1u << (sel >> 6));
-  }
-  // weights: softmax over the selection (norm) or full softmax entries
-  const float vmax = sel_v[0];
-  float denom = 0.f;
-  if (norm) {
-    for (int k = 0; k < K; ++k) denom += expf(sel_v[k] - vmax);
-  } else {
+  });
+  if (!norm) {
     float part = 0.f;
-    for (int e = lane; e < E; e += 64) part += expf(l[e] - vmax);
+#pragma unroll
+    for (int m = 0; m < MP; ++m)
+      if (lane + 64 * m < E) part += expf(v[m] - first);
     denom = group_sum<64>(part);
   }
   if (lane < K) {
-    float mine = 0.f;
-    int mine_e = 0;
-    for (int k = 0; k < K; ++k)
-      if (k == lane) {
-        mine = sel_v[k];
-        mine_e = sel_e[k];
-      }
     idx[size_t(t) * K + lane] = mine_e;
-    w[size_t(t) * K + lane] = expf(mine - vmax) / denom;
+    w[size_t(t) * K + lane] = mine / denom;
   }
   if (n_shared && lane == 0) sw[t] = sigmoid_f(sg_logit[t]);
 }
