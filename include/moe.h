@@ -251,6 +251,82 @@ MOE_API moe_status_t prerouter_predict(const uint16_t* W1, const uint16_t* W2, i
                                int32_t* pred_idx, float* pred_logits, void* ws, size_t ws_bytes,
                                void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Expert pool.  [P2] "SSD 专家卸载 · Prerouter 路由预测", expert-pool and
+ * Prerouter paragraphs: a streaming pool caches recently used experts and
+ * loads the experts the Prerouter predicts; layer N's prediction on the
+ * current token is for layer N+1 of the next token and is committed at the
+ * step boundary, so loads overlap the next step's compute.
+ *
+ * Here every layer has n_slots HBM slots; the master copy of all experts is
+ * pinned host memory; kernels find expert e of a layer through the device
+ * slot table (moe_experts_t.expert_to_slot) and read a non-resident expert
+ * from the host copy directly, so results do not depend on the pool state.
+ *
+ * moe_lru_*: the host-only planner (no device work, usable without a GPU).
+ * A plan step takes, per layer, the K experts executed in the step just
+ * finished and Kp predicted experts (entries < 0: none), and returns fills:
+ *   - executed and predicted experts that are resident become most recent;
+ *   - fill candidates are the predicted experts that are not resident, then
+ *     the executed ones that missed, each once, at most max_fills per layer
+ *     (max_fills < 0: no limit);
+ *   - a fill takes a free slot, else the least recently used slot whose
+ *     expert was neither executed nor predicted in this step (ties: lowest
+ *     slot); with no such slot the layer's remaining candidates are skipped.
+ * fills[] are ordered by layer, then candidate order.
+ */
+typedef struct moe_lru moe_lru_t;
+typedef struct {
+  int32_t layer, expert, slot, evicted; /* evicted: expert that left the slot, or -1 */
+} moe_pool_fill_t;
+
+MOE_API moe_status_t moe_lru_create(int32_t n_layers, int32_t E, int32_t n_slots, moe_lru_t** out);
+MOE_API void moe_lru_destroy(moe_lru_t* l);
+/* executed: host int32 [n_layers][K]; predicted: host int32 [n_layers][Kp]
+ * or NULL with Kp = 0.  fills: host array of max_out entries; *n_out gets
+ * the number of fills (MOE_EINVAL if it exceeds max_out; the plan is still
+ * applied to the planner state). */
+MOE_API moe_status_t moe_lru_plan(moe_lru_t* l, const int32_t* executed, int32_t K,
+                                  const int32_t* predicted, int32_t Kp, int32_t max_fills,
+                                  moe_pool_fill_t* fills, int32_t max_out, int32_t* n_out);
+/* The planner's current slot of every expert of `layer` (host int32 [E]). */
+MOE_API moe_status_t moe_lru_table(const moe_lru_t* l, int32_t layer, int32_t* expert_to_slot);
+MOE_API moe_status_t moe_lru_stats(const moe_lru_t* l, unsigned long long* fills,
+                                   unsigned long long* evictions);
+
+/* moe_pool_*: the planner plus the device side.  The caller owns
+ *   device_slots  device [n_layers][n_slots][blob_bytes],
+ *   device_table  device int32 [n_layers][E] (set to -1 here, synchronously
+ *                 on `stream`),
+ *   host_blobs    pinned host [n_layers][E][blob_bytes], device-visible
+ *                 (checked with hipHostGetDevicePointer: MOE_EINVAL if not);
+ * the pool owns pinned staging rows and one event per layer.  Not
+ * thread-safe; one pool per stream pair. */
+typedef struct moe_pool moe_pool_t;
+MOE_API moe_status_t moe_pool_create(int32_t n_layers, int32_t E, int32_t n_slots, size_t blob_bytes,
+                                     void* device_slots, int32_t* device_table,
+                                     const void* host_blobs, void* stream, moe_pool_t** out);
+MOE_API void moe_pool_destroy(moe_pool_t* p);
+/* The moe_experts_t of one layer (counters may be NULL). */
+MOE_API moe_status_t moe_pool_layer(const moe_pool_t* p, int32_t layer, unsigned long long* counters,
+                                    moe_experts_t* out);
+/* Plan one step (as moe_lru_plan) and enqueue it on side_stream: per layer
+ * with fills, the table row without the evicted experts, event inv[layer],
+ * the blob copies, then the table row with the new slots.  Waits (host) for
+ * side_stream's previous work first.  Call it only after every kernel of the
+ * step that produced `executed` has completed. */
+MOE_API moe_status_t moe_pool_update(moe_pool_t* p, const int32_t* executed, int32_t K,
+                                     const int32_t* predicted, int32_t Kp, int32_t max_fills,
+                                     void* side_stream, int32_t* n_fills);
+/* Make `stream` wait for the last update's invalidation of `layer` (no-op if
+ * the layer had no fills since the last wait).  Call before a kernel that
+ * reads the layer's table. */
+MOE_API moe_status_t moe_pool_wait_layer(moe_pool_t* p, int32_t layer, void* stream);
+/* Host wait for all enqueued fills. */
+MOE_API moe_status_t moe_pool_sync(moe_pool_t* p, void* side_stream);
+/* The pool's planner (for moe_lru_table / moe_lru_stats). */
+MOE_API const moe_lru_t* moe_pool_lru(const moe_pool_t* p);
+
 #ifdef __cplusplus
 }
 #endif

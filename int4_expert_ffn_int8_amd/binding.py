@@ -32,6 +32,10 @@ class MoeDims(ctypes.Structure):
                 ("n_shared", c_i32), ("norm_topk", c_i32), ("lora_scale", c_f32)]
 
 
+class MoePoolFill(ctypes.Structure):
+    _fields_ = [("layer", c_i32), ("expert", c_i32), ("slot", c_i32), ("evicted", c_i32)]
+
+
 class MoeExperts(ctypes.Structure):
     _fields_ = [("slots", c_vp), ("n_slots", c_i32), ("expert_to_slot", c_vp),
                 ("host_blobs", c_vp), ("counters", c_vp)]
@@ -58,6 +62,22 @@ _SIGS = {
                                  ctypes.POINTER(MoeExperts), c_vp, c_vp, c_i32, c_i32, c_f32,
                                  c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "prerouter_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32]),
+    "moe_lru_create": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_vp)]),
+    "moe_lru_destroy": (None, [c_vp]),
+    "moe_lru_plan": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_vp, c_i32,
+                             ctypes.POINTER(c_i32)]),
+    "moe_lru_table": (c_i32, [c_vp, c_i32, c_vp]),
+    "moe_lru_stats": (c_i32, [c_vp, ctypes.POINTER(ctypes.c_ulonglong),
+                              ctypes.POINTER(ctypes.c_ulonglong)]),
+    "moe_pool_create": (c_i32, [c_i32, c_i32, c_i32, c_sz, c_vp, c_vp, c_vp, c_vp,
+                                ctypes.POINTER(c_vp)]),
+    "moe_pool_destroy": (None, [c_vp]),
+    "moe_pool_layer": (c_i32, [c_vp, c_i32, c_vp, ctypes.POINTER(MoeExperts)]),
+    "moe_pool_update": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_vp,
+                                ctypes.POINTER(c_i32)]),
+    "moe_pool_wait_layer": (c_i32, [c_vp, c_i32, c_vp]),
+    "moe_pool_sync": (c_i32, [c_vp, c_vp]),
+    "moe_pool_lru": (c_vp, [c_vp]),
     "prerouter_predict": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp,
                                   c_vp, c_vp, c_sz, c_vp]),
 }
@@ -68,6 +88,9 @@ HEADER_SYMBOLS = [
     "moe_route", "moe_expert_forward", "moe_combine", "moe_rmsnorm",
     "moe_block_decode_workspace_bytes", "moe_workspace_init", "moe_block_decode",
     "prerouter_workspace_bytes", "prerouter_predict",
+    "moe_lru_create", "moe_lru_destroy", "moe_lru_plan", "moe_lru_table", "moe_lru_stats",
+    "moe_pool_create", "moe_pool_destroy", "moe_pool_layer", "moe_pool_update",
+    "moe_pool_wait_layer", "moe_pool_sync", "moe_pool_lru",
 ]
 
 DECODE_NORM_INPUT = 1
@@ -206,3 +229,112 @@ def moe_block_decode(d, gate_q, gate_s, sgate_q, sgate_s, routed: MoeExperts, sh
                                    ptr(out), ptr(ws),
                                    ws.numel() * ws.element_size() if ws is not None else 0,
                                    stream_ptr(stream)))
+
+
+# ---- expert pool ------------------------------------------------------------
+def _i32_array(a):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data
+
+
+class MoeLru:
+    """Host LRU planner (moe_lru_*); usable without a GPU."""
+
+    def __init__(self, n_layers: int, E: int, n_slots: int):
+        self.h = None
+        h = c_vp()
+        _check(load().moe_lru_create(n_layers, E, n_slots, ctypes.byref(h)))
+        self.h, self.n_layers, self.E, self.n_slots = h, n_layers, E, n_slots
+
+    def plan(self, executed, predicted=None, max_fills: int = -1):
+        """executed int [n_layers, K], predicted int [n_layers, Kp] or None;
+        returns a list of (layer, expert, slot, evicted)."""
+        import numpy as np
+        ex, exp = _i32_array(executed)
+        K = ex.shape[1] if ex.ndim == 2 else 0
+        if predicted is None:
+            pr, prp, Kp = None, None, 0
+        else:
+            pr, prp = _i32_array(predicted)
+            Kp = pr.shape[1]
+        cap = self.n_layers * (K + Kp) + 1
+        fills = (MoePoolFill * cap)()
+        n = c_i32(0)
+        _check(load().moe_lru_plan(self.h, exp, K, prp, Kp, max_fills, fills, cap, ctypes.byref(n)))
+        return [(f.layer, f.expert, f.slot, f.evicted) for f in fills[:n.value]]
+
+    def table(self, layer: int):
+        import numpy as np
+        out = np.empty(self.E, np.int32)
+        _check(load().moe_lru_table(self.h, layer, out.ctypes.data))
+        return out
+
+    def stats(self):
+        f, e = ctypes.c_ulonglong(0), ctypes.c_ulonglong(0)
+        _check(load().moe_lru_stats(self.h, ctypes.byref(f), ctypes.byref(e)))
+        return int(f.value), int(e.value)
+
+    def close(self):
+        if getattr(self, "h", None):
+            load().moe_lru_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        self.close()
+
+
+class MoePool:
+    """Device expert pool (moe_pool_*).  The caller keeps slots, table and
+    host_blobs alive for the pool's lifetime."""
+
+    def __init__(self, n_layers, E, n_slots, blob_bytes, slots, table, host_blobs, stream=None):
+        self.h = None
+        h = c_vp()
+        _check(load().moe_pool_create(n_layers, E, n_slots, blob_bytes, ptr(slots), ptr(table),
+                                      ptr(host_blobs), stream_ptr(stream), ctypes.byref(h)))
+        self.h, self.n_layers, self.E, self.n_slots = h, n_layers, E, n_slots
+        self._keep = (slots, table, host_blobs)
+
+    def layer(self, layer: int, counters=None) -> MoeExperts:
+        out = MoeExperts()
+        _check(load().moe_pool_layer(self.h, layer, ptr(counters), ctypes.byref(out)))
+        return out
+
+    def update(self, executed, predicted=None, max_fills: int = -1, side_stream=None) -> int:
+        ex, exp = _i32_array(executed)
+        K = ex.shape[1]
+        if predicted is None:
+            pr, prp, Kp = None, None, 0
+        else:
+            pr, prp = _i32_array(predicted)
+            Kp = pr.shape[1]
+        n = c_i32(0)
+        _check(load().moe_pool_update(self.h, exp, K, prp, Kp, max_fills, stream_ptr(side_stream),
+                                      ctypes.byref(n)))
+        return n.value
+
+    def wait_layer(self, layer: int, stream=None) -> None:
+        _check(load().moe_pool_wait_layer(self.h, layer, stream_ptr(stream)))
+
+    def sync(self, side_stream=None) -> None:
+        _check(load().moe_pool_sync(self.h, stream_ptr(side_stream)))
+
+    def table(self, layer: int):
+        import numpy as np
+        out = np.empty(self.E, np.int32)
+        _check(load().moe_lru_table(load().moe_pool_lru(self.h), layer, out.ctypes.data))
+        return out
+
+    def stats(self):
+        f, e = ctypes.c_ulonglong(0), ctypes.c_ulonglong(0)
+        _check(load().moe_lru_stats(load().moe_pool_lru(self.h), ctypes.byref(f), ctypes.byref(e)))
+        return int(f.value), int(e.value)
+
+    def close(self):
+        if getattr(self, "h", None):
+            load().moe_pool_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        self.close()

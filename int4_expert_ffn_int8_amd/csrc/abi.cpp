@@ -184,7 +184,7 @@ extern "C" moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_expert
   a.shared_blob = static_cast<const uint8_t*>(shared_blob);
   a.blobptr = reinterpret_cast<unsigned long long*>(wsb + W.blobptr);
   a.u = reinterpret_cast<float*>(wsb + W.u);
-  a.h = reinterpret_cast<uint16_t*>(wsb + W.h);
+  a.h = reinterpret_cast<float*>(wsb + W.h);
   a.vpart = reinterpret_cast<float*>(wsb + W.vpart);
   a.y = y;
   return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)), fn);
@@ -305,6 +305,7 @@ extern "C" moe_status_t moe_block_decode(const moe_dims_t* d, const int8_t* gate
   a.wts = reinterpret_cast<tword_t*>(wsb + W.wts);
   a.u = reinterpret_cast<tword_t*>(wsb + W.u);
   a.h = reinterpret_cast<tword_t*>(wsb + W.h);
+  a.hexp = reinterpret_cast<tword_t*>(wsb + W.hexp);
   a.vpart = reinterpret_cast<tword_t*>(wsb + W.vpart);
   return hip_status(launch_fused(a, static_cast<hipStream_t>(stream)), fn);
 }

@@ -202,9 +202,8 @@ __global__ void __launch_bounds__(256) k_gateup_decode(DecodeArgs a) {
   if (tid < U::JW) {
     const int w = tid / U::JPW, jl = tid % U::JPW;
     const float hv = silu_f(lds_a[w][2 * jl]) * lds_a[w][2 * jl + 1];
-    const uint16_t hb = f32_to_f16_sat(hv);
-    a.h[size_t(p) * a.I + blk * U::JW + tid] = hb;
-    lds_h[tid] = f16_to_f32(hb);
+    a.h[size_t(p) * a.I + blk * U::JW + tid] = hv;
+    lds_h[tid] = hv;
   }
   __syncthreads();
   if (r == 0) return;
@@ -257,9 +256,32 @@ __global__ void __launch_bounds__(256) k_down_decode(DecodeArgs a, int NB) {
     for (int b = 0; b < NB; ++b) s += vp[size_t(b) * r];
     vs[threadIdx.x] = s;
   }
+  // h slices as fp16(h * 2^-e), one exponent per 32-column slice
   uint32_t xw[G::SL][16];
   float xs[G::SL];
-  load_vec_slices<I, true>(a.h + size_t(p) * I, sub, xw, xs);
+  int xe[G::SL];
+#pragma unroll
+  for (int c = 0; c < G::SL; ++c) {
+    const float4* hp = reinterpret_cast<const float4*>(a.h + size_t(p) * I + 32 * sub + 2048 * c);
+    float hv[32];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 v = hp[k];
+      hv[4 * k] = v.x; hv[4 * k + 1] = v.y; hv[4 * k + 2] = v.z; hv[4 * k + 3] = v.w;
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) m = fmaxf(m, fabsf(hv[k]));
+    xe[c] = h_block_exp(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      f16x2_t pr = {_Float16(ldexpf(hv[2 * k], -xe[c])), _Float16(ldexpf(hv[2 * k + 1], -xe[c]))};
+      xw[c][k] = __builtin_bit_cast(uint32_t, pr);
+      sum += float(pr[0]) + float(pr[1]);
+    }
+    xs[c] = sum;
+  }
   __syncthreads();
   const uint16_t* Bd = reinterpret_cast<const uint16_t*>(blob + a.L.b_dn);
 #pragma unroll
@@ -267,7 +289,8 @@ __global__ void __launch_bounds__(256) k_down_decode(DecodeArgs a, int NB) {
     const int row = row0 + i * G::RPL + lane / G::LPR;
     float part = 0.f;
 #pragma unroll
-    for (int c = 0; c < G::SL; ++c) part += int4_slice_dot<true>(q[i][c], sbw[i][c], xw[c], xs[c]);
+    for (int c = 0; c < G::SL; ++c)
+      part += ldexpf(int4_slice_dot<true>(q[i][c], sbw[i][c], xw[c], xs[c]), xe[c]);
     if (row < H)
       for (int rr = sub; rr < r; rr += G::LPR)
         part = fmaf(a.lam * bf16_to_f32(Bd[size_t(row) * r + rr]), vs[rr], part);

@@ -148,6 +148,14 @@ struct Geo {
   static constexpr int SL = (IN / 32) > 64 ? (IN / 2048) : 1;
 };
 
+// Exponent e >= 0 of a block of activations stored as fp16(v * 2^-e): the
+// smallest shift that keeps the block's largest magnitude m below 2^15, so
+// fp16 (largest finite 65504) never saturates; e = 0 when m < 2^15.
+__device__ __forceinline__ int h_block_exp(float m) {
+  if (!(m >= 32768.0f)) return 0;
+  return min(ilogbf(m) - 14, 126);
+}
+
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
 

@@ -51,14 +51,15 @@ struct FusedArgs {
   tword_t* route;   // [T][K]       expert ids
   tword_t* wts;     // [T][K + 1]   routing weights; column K: shared gate
   tword_t* u;       // [P][2r]      A_gate x, A_up x
-  tword_t* h;       // [P][I / 2]   fp16 pairs
+  tword_t* h;       // [P][I / 2]   fp16 pairs of h * 2^-e
+  tword_t* hexp;    // [P][I / 32]  e of each 32-column block of h
   tword_t* vpart;   // [P][I / kFusedJW][r]
   // grid layout (filled by the launcher)
   int nR, nWA, nBG, nD, base_la, base_gu, base_dn, total;
 };
 
 struct FusedWs {
-  size_t sync, logits, route, wts, u, h, vpart, total;
+  size_t sync, logits, route, wts, u, h, hexp, vpart, total;
 };
 
 inline FusedWs fused_ws_layout(int T, int E, int K, int S, int I, int r) {
@@ -71,6 +72,7 @@ inline FusedWs fused_ws_layout(int T, int E, int K, int S, int I, int r) {
   W.wts = o;    o = align256(o + size_t(T) * (K + 1) * 8);
   W.u = o;      o = align256(o + P * 2 * r * 8);
   W.h = o;      o = align256(o + P * (I / 2) * 8);
+  W.hexp = o;   o = align256(o + P * (I / 32) * 8);
   W.vpart = o;  o = align256(o + P * (I / kFusedJW) * r * 8);
   W.total = o;
   return W;

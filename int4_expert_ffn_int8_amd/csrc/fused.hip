@@ -386,15 +386,24 @@ __device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, 
     for (int i = 0; i < NL; ++i) lds_a[wave * NR + i * RPL + lane / G::LPR] = part[i];
   }
   __syncthreads();
+  float* lds_hraw = lds_h + JW;  // [JW]
   if (tid < JW) {
     const int w = tid / JPW, jl = tid % JPW;
-    const float hv = silu_f(lds_a[w * NR + 2 * jl]) * lds_a[w * NR + 2 * jl + 1];
-    lds_h[tid] = f16_to_f32(f32_to_f16_sat(hv));
+    lds_hraw[tid] = silu_f(lds_a[w * NR + 2 * jl]) * lds_a[w * NR + 2 * jl + 1];
   }
   __syncthreads();
-  if (tid < JW / 2) {  // h as fp16 pairs, one tagged word per pair
-    f16x2_t pr = {_Float16(lds_h[2 * tid]), _Float16(lds_h[2 * tid + 1])};
+  // this block of h is one 32-column slice of the down rows: it is stored as
+  // fp16(h * 2^-e) with one exponent e per block (e = 0 unless |h| >= 2^15)
+  float hmax = 0.f;
+  for (int j = 0; j < JW; ++j) hmax = fmaxf(hmax, fabsf(lds_hraw[j]));
+  const int hexp = h_block_exp(hmax);
+  if (tid < JW) lds_h[tid] = ldexpf(f16_to_f32(f32_to_f16_sat(ldexpf(lds_hraw[tid], -hexp))), hexp);
+  __syncthreads();
+  if (tid < JW / 2) {  // fp16 pairs of h * 2^-e, one tagged word per pair
+    f16x2_t pr = {_Float16(ldexpf(lds_h[2 * tid], -hexp)), _Float16(ldexpf(lds_h[2 * tid + 1], -hexp))};
     st_dev(&a.h[p * (a.I / 2) + blk * (JW / 2) + tid], tw(tag, __builtin_bit_cast(uint32_t, pr)));
+  } else if (tid == JW / 2) {
+    st_dev(&a.hexp[p * (a.I / JW) + blk], tw(tag, uint32_t(hexp)));
   }
   if (r > 0) {  // this block's partial of v = A_down h
     const int NB = a.I / JW;
@@ -410,13 +419,16 @@ __device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, 
 
 // ---------------------------------------------------------------------------
 template <int H, int I>
-__device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* lds_hs, float* lds_v,
+__device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* lds_hs, int* lds_he,
+                          float* lds_v,
                           float* lds_wt, int* lds_idx) {
   using G = Geo<I>;
   constexpr int RPL = G::RPL;
   constexpr int NB = I / kFusedJW;  // partials of A_down h per pair
   constexpr int MAXH = (kFusedMaxP * I / 2 + 255) / 256;
   constexpr int MAXC = (kFusedMaxP * kMaxR * 16 + 255) / 256;
+  constexpr int MAXE = (kFusedMaxP * I / 32 + 255) / 256;
+  static_assert(kFusedJW == 32, "one h exponent per 32-column slice of a down row");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane % G::LPR;
   const int tid = threadIdx.x;
   const int row = d * 4 * RPL + wave * RPL + lane / G::LPR;
@@ -470,6 +482,8 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
   tword_t hv[MAXH], vp[MAXC];
   float wtv = 0.f;
   const int nh = P * (I / 2);
+  const int ne = P * (I / 32);
+  tword_t hev[MAXE];
   const int tw_t = min(tid, P - 1) / KS, tw_k = min(tid, P - 1) % KS;
   const int tw_i = tw_t * (a.K + 1) + (tw_k < a.K ? tw_k : a.K);
   // partial of v read by slot c of this thread: (pair, rank, block < 16);
@@ -491,12 +505,16 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
 #pragma unroll
     for (int k = 0; k < MAXH; ++k) hv[k] = ld_dev(&a.h[min(tid + 256 * k, nh - 1)]);
 #pragma unroll
+    for (int k = 0; k < MAXE; ++k) hev[k] = ld_dev(&a.hexp[min(tid + 256 * k, ne - 1)]);
+#pragma unroll
     for (int c = 0; c < MAXC; ++c) vp[c] = ld_dev(&vsrc[vidx[c]]);
     const tword_t w = ld_dev(&a.wts[tw_i]);
     unsigned bad = unsigned(tid < P) & unsigned(!has_tag(w, tag));
     wtv = wf(w);
 #pragma unroll
     for (int k = 0; k < MAXH; ++k) bad |= unsigned(tid + 256 * k < nh) & unsigned(!has_tag(hv[k], tag));
+#pragma unroll
+    for (int k = 0; k < MAXE; ++k) bad |= unsigned(tid + 256 * k < ne) & unsigned(!has_tag(hev[k], tag));
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) bad |= ((vneed >> c) & 1u) & unsigned(!has_tag(vp[c], tag));
     if (round_done(a, bad == 0, n)) break;
@@ -542,6 +560,9 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
     }
   }
   if (tid < P) lds_wt[tid] = wtv;
+#pragma unroll
+  for (int k = 0; k < MAXE; ++k)
+    if (tid + 256 * k < ne) lds_he[tid + 256 * k] = int(uint32_t(hev[k]));
   __syncthreads();
   float o[kFusedMaxT];
 #pragma unroll
@@ -557,6 +578,7 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
       hw[4 * k] = v.x; hw[4 * k + 1] = v.y; hw[4 * k + 2] = v.z; hw[4 * k + 3] = v.w;
     }
     float y = slice_dot<true>(q[p], sbw[p], hw, lds_hs[p * (I / 32) + sub]);
+    y = ldexpf(y, lds_he[p * (I / 32) + sub]);
     if (sub < r) y = fmaf(a.lam * bf16_to_f32(bdraw[p]), lds_v[p * kMaxR + sub], y);
     y = group_sum<G::LPR>(y);
     const int t = p / KS;
@@ -581,6 +603,7 @@ template <int H, int I>
 __global__ void __launch_bounds__(256) k_fused_decode(FusedArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_hh[kFusedMaxP * I];
   __shared__ float lds_hs[kFusedMaxP * I / 32];
+  __shared__ int lds_he[kFusedMaxP * I / 32];
   __shared__ __attribute__((aligned(16))) float lds_f[kFusedMaxP * kMaxR + 160];
   __shared__ float lds_wt[kFusedMaxP];
   __shared__ int lds_i[kFusedMaxP];
@@ -594,7 +617,7 @@ __global__ void __launch_bounds__(256) k_fused_decode(FusedArgs a) {
     const int i = b - a.base_gu;
     role_gate_up<H>(a, i / a.nBG, i % a.nBG, lds_f, lds_i);
   } else {
-    role_down<H, I>(a, b - a.base_dn, lds_hh, lds_hs, lds_f, lds_wt, lds_i);
+    role_down<H, I>(a, b - a.base_dn, lds_hh, lds_hs, lds_he, lds_f, lds_wt, lds_i);
   }
   // the last workgroup out starts the next epoch
   __syncthreads();

@@ -36,7 +36,7 @@ struct DecodeArgs {
   // workspace
   unsigned long long* blobptr;  // [NP]
   float* u;                     // [NP, 2r]
-  uint16_t* h;                  // [NP, I] fp16
+  float* h;                     // [NP, I]
   float* vpart;                 // [NP, I/JW, r]
   float* y;                     // [NP, H]
 };

@@ -15,7 +15,7 @@ struct WsLayout {
   // decode expert path
   size_t blobptr;  // u64 [NP]    resolved blob address per (token, slot)
   size_t u;        // fp32 [NP, 2r]
-  size_t h;        // fp16 [NP, I]
+  size_t h;        // fp32 [NP, I]
   size_t vpart;    // fp32 [NP, I/JW, r]
   // prefill grouping and grouped GEMMs (NR = T*K + n_shared*T sorted rows)
   size_t chunk_hist;  // int32 [nch, E]
@@ -39,7 +39,7 @@ inline WsLayout ws_layout(const moe_dims_t& d, int T, bool prefill) {
   W.sg = o;      o = align256(o + size_t(T) * 4);
   W.blobptr = o; o = align256(o + NP * 8);
   W.u = o;       o = align256(o + NP * 2 * d.r * 4);
-  W.h = o;       o = align256(o + NP * d.I * 2);
+  W.h = o;       o = align256(o + NP * d.I * 4);
   W.vpart = o;   o = align256(o + NP * nb * d.r * 4);
   const size_t TK = size_t(T) * d.K;
   const size_t nch = prefill ? (TK + kGroupChunk - 1) / kGroupChunk : 0;

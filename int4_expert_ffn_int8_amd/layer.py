@@ -139,3 +139,112 @@ class MoeLayer:
         """Sticky timeout flag of the fused kernel (0 = every wait completed)."""
         o = B.DECODE_ERR_OFFSET
         return int(fb["ws"][o:o + 4].view(torch.int32).item())
+
+
+class MoeStack:
+    """A decode stack of MoE layers, one token step at a time.
+
+    Layer l computes h <- h + MoE_l(RMSNorm(h)) in one fused launch.  With
+    Prerouter heads, head l reads layer l's output and predicts the experts
+    of layer l + 1 for the next step ([P2] Prerouter paragraph: predictions
+    cross one layer and one token and are committed at the step boundary).
+    With a pool, routed experts live in per-layer HBM slots fed from a pinned
+    host master copy; `end_step` commits the step (executed + predicted
+    experts) to the pool, whose fills then overlap the next step.
+
+    routers: per layer dict(router_q, router_s, sgate_q, sgate_s);
+    shared_blobs: device uint8 [L, blob] or None; routed: device uint8
+    [L, E, blob] (all resident) or None with `host_blobs` (pinned uint8
+    [L, E, blob]) and `pool_slots`; prerouter: per-layer (W1, W2) device bf16
+    for layers 0 .. L-2, or None.
+    """
+
+    def __init__(self, H, I, E, K, r, n_shared, lora_scale, routers, shared_blobs, routed=None,
+                 host_blobs=None, pool_slots=0, prerouter=None, pred_k=0, eps=1e-6,
+                 max_fills=-1, device="cuda"):
+        self.H, self.I, self.E, self.K, self.r, self.S = H, I, E, K, r, n_shared
+        self.L = len(routers)
+        self.d = B.dims(H, I, E, K, r, n_shared, lora_scale, 1)
+        self.eps, self.device, self.max_fills = eps, device, max_fills
+        self.blob_bytes = B.moe_expert_blob_bytes(H, I, r)
+        dv = device
+        self.routers = [{k: dev(v.reshape(-1) if k.startswith("sgate") else v, dv)
+                         for k, v in R.items()} for R in routers]
+        self.shared = shared_blobs
+        self.pool = None
+        self.counters = torch.zeros((self.L, 2), dtype=torch.int64, device=dv)
+        if routed is not None:
+            self.routed = routed
+            self.experts = [B.experts_struct(routed[l], E) for l in range(self.L)]
+        else:
+            assert host_blobs is not None and pool_slots > 0
+            self.routed = None
+            self.host_blobs = host_blobs
+            self.slots = torch.empty((self.L, pool_slots, self.blob_bytes), dtype=torch.uint8, device=dv)
+            self.table = torch.empty((self.L, E), dtype=torch.int32, device=dv)
+            self.side = torch.cuda.Stream(device=dv)
+            self.pool = B.MoePool(self.L, E, pool_slots, self.blob_bytes, self.slots, self.table,
+                                  host_blobs)
+            self.experts = [self.pool.layer(l, self.counters[l]) for l in range(self.L)]
+        self.prerouter = prerouter
+        self.pred_k = pred_k
+        T = 1
+        self.ws = torch.empty((B.moe_block_decode_workspace_bytes(self.d, T),), dtype=torch.uint8,
+                              device=dv)
+        B.moe_workspace_init(self.ws)
+        self.idx = torch.empty((self.L, T, K), dtype=torch.int32, device=dv)
+        self.w = torch.empty((self.L, T, K), dtype=torch.float32, device=dv)
+        self.h = [torch.empty((T, H), dtype=torch.int16, device=dv) for _ in range(2)]
+        if prerouter is not None:
+            D = prerouter[0][0].shape[0]
+            self.pr_ws = torch.empty((B.prerouter_workspace_bytes(D, E, T),), dtype=torch.uint8,
+                                     device=dv)
+            self.pred = torch.full((self.L, T, pred_k), -1, dtype=torch.int32, device=dv)
+        # step-boundary copies for the pool planner
+        self.idx_host = torch.empty((self.L, K), dtype=torch.int32, pin_memory=True)
+        self.pred_host = torch.full((self.L, max(pred_k, 1)), -1, dtype=torch.int32,
+                                    pin_memory=True)
+        self.done = torch.cuda.Event()
+
+    def layer_forward(self, l, h_in, out, stream=None):
+        R = self.routers[l]
+        if self.pool is not None:
+            self.pool.wait_layer(l, stream)
+        B.moe_block_decode(self.d, R["router_q"], R["router_s"], R.get("sgate_q"),
+                           R.get("sgate_s"), self.experts[l],
+                           self.shared[l] if self.S else None, h_in, 1,
+                           B.DECODE_NORM_INPUT | B.DECODE_RESIDUAL, self.eps, self.idx[l],
+                           self.w[l], out, self.ws, stream)
+
+    def step(self, x, stream=None):
+        """One token through every layer; returns the output hidden state."""
+        cur = x
+        for l in range(self.L):
+            out = self.h[l % 2]
+            self.layer_forward(l, cur, out, stream)
+            if self.prerouter is not None and l + 1 < self.L:
+                W1, W2 = self.prerouter[l]
+                B.prerouter_predict(W1, W2, self.H, W1.shape[0], self.E, self.pred_k, out, 1,
+                                    self.pred[l + 1], None, self.pr_ws, stream)
+            cur = out
+        return cur
+
+    def end_step(self, stream=None):
+        """Commit the step to the pool (no-op without a pool): waits for the
+        step's kernels, then plans and enqueues the fills on the side stream."""
+        if self.pool is None:
+            return 0
+        s = torch.cuda.current_stream() if stream is None else stream
+        with torch.cuda.stream(s):
+            self.idx_host.copy_(self.idx.view(self.L, self.K), non_blocking=True)
+            if self.prerouter is not None:
+                self.pred_host.copy_(self.pred.view(self.L, self.pred_k), non_blocking=True)
+        self.done.record(s)
+        self.done.synchronize()
+        pred = self.pred_host.numpy() if self.prerouter is not None else None
+        return self.pool.update(self.idx_host.numpy(), pred, self.max_fills, self.side)
+
+    def hit_counts(self):
+        """(lookups served from a slot, all lookups) summed over layers."""
+        c = self.counters.sum(0).tolist()
+        return int(c[0]), int(c[1])

@@ -102,3 +102,30 @@ def test_fused_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(fb["out"], eager)
     assert L.fused_error_word(fb) == 0
+
+
+@pytest.mark.parametrize("path", ["fused", "three_call"])
+def test_large_activations_keep_full_range(path):
+    # x * 2^8 drives the SwiGLU outputs h far above the fp16 range (|h| up to
+    # ~1e6); the decode paths store h as fp16 with a power-of-two exponent
+    # per 32-column block, so the result must still match the oracle
+    from int4_expert_ffn_int8_amd.layer import dev
+    w = synth.workload(0)
+    L, router, experts, shared = _layer(w)
+    xb = synth.tokens(w, 5, T=2)
+    x = O.round_bf16(O.bf16_to_f64(xb) * 256.0)  # exact: power-of-two scaling
+    ref, parts = O.moe_block(w, router, lambda e: experts[e], x, shared=shared,
+                             return_parts=True)
+    _, hid = O.expert_forward(shared, O.bf16_to_f64(x), w["lora_scale"], return_hidden=True)
+    assert np.abs(hid).max() > 1e5  # far outside the fp16 range
+    if path == "fused":
+        fb = L.fused_buffers(2)
+        out = L.decode_fused(dev(x), fb)
+        idx = fb["idx"]
+    else:
+        b = L.buffers(2)
+        out = L.forward(dev(x), b)
+        idx = b["idx"]
+    torch.cuda.synchronize()
+    assert idx.cpu().numpy().tolist() == parts["idx"].tolist()
+    assert_bf16_output_close(_bits(out), ref, f"large activations ({path})")
