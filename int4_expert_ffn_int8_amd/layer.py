@@ -52,7 +52,8 @@ class MoeLayer:
     """One MoE block whose routed experts all live in HBM (or in a pool)."""
 
     def __init__(self, H, I, E, K, r, n_shared, lora_scale, router: dict, experts,
-                 shared: dict | None, norm_topk: int = 1, device="cuda", blobs=None):
+                 shared: dict | None, norm_topk: int = 1, device="cuda", blobs=None,
+                 shared_blob=None):
         self.H, self.I, self.E, self.K, self.r = H, I, E, K, r
         self.S = n_shared
         self.d = B.dims(H, I, E, K, r, n_shared, lora_scale, norm_topk)
@@ -65,7 +66,12 @@ class MoeLayer:
         if blobs is None:
             blobs = pack_experts(H, I, r, experts)
         self.slots = dev(blobs, device) if blobs is not None else None
-        self.shared_blob = dev(pack_experts(H, I, r, [shared])[0], device) if n_shared else None
+        if not n_shared:
+            self.shared_blob = None
+        elif shared_blob is not None:  # already packed
+            self.shared_blob = dev(np.ascontiguousarray(shared_blob), device)
+        else:
+            self.shared_blob = dev(pack_experts(H, I, r, [shared])[0], device)
         self.experts = B.experts_struct(self.slots, E)
 
     def buffers(self, T: int, prefill: bool = False) -> dict:
