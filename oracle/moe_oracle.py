@@ -19,8 +19,7 @@ definition that fixes the FFN form and the routing order):
 Everything is computed in float64.  bf16 inputs are widened exactly; the only
 roundings are the ones that define an interface: bf16 block/stack outputs.
 
-Readings where the pages are silent (each is listed with its reason in the
-design notes):
+Readings where the pages are silent:
   * int4 dequant is affine per 64 consecutive input columns of one output row:
     w = s*q + b, q in {0..15}, s and b bf16.
   * int8 gates are symmetric: w = s*q, fp32 scale per 64 columns.
