@@ -160,13 +160,22 @@ extern "C" moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_expert
     g.gblob = reinterpret_cast<const unsigned long long*>(wsb + W.gblob);
     g.L = L;
     g.x = x;
-    g.hs = g.hs_out = reinterpret_cast<uint16_t*>(wsb + W.phs);
+    uint16_t* x16 = reinterpret_cast<uint16_t*>(wsb + W.x16);
+    int32_t* ex = reinterpret_cast<int32_t*>(wsb + W.ex);
+    uint16_t* hs16 = reinterpret_cast<uint16_t*>(wsb + W.hs16);
+    int32_t* eh = reinterpret_cast<int32_t*>(wsb + W.eh);
+    g.x16 = x16;
+    g.ex = ex;
+    g.hf = reinterpret_cast<float*>(wsb + W.hf);
+    g.hmax = reinterpret_cast<uint32_t*>(wsb + W.hmax);
+    g.hs = hs16;
+    g.eh = eh;
     g.u = g.u_out = reinterpret_cast<uint16_t*>(wsb + W.pu);
     g.ud = g.ud_out = reinterpret_cast<uint16_t*>(wsb + W.pud);
     g.y = y;
     return hip_status(launch_prefill_experts(g, counts, src,
-                                             static_cast<const uint8_t*>(shared_blob),
-                                             static_cast<hipStream_t>(stream)),
+                                             static_cast<const uint8_t*>(shared_blob), x16, ex,
+                                             hs16, eh, static_cast<hipStream_t>(stream)),
                       fn);
   }
   DecodeArgs a;

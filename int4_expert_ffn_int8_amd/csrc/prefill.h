@@ -12,6 +12,10 @@ constexpr int kGroupChunk = 1024;  // pairs per grouping workgroup
 constexpr int kPrefillBM = 128;    // rows (pairs/tokens) per expert-GEMM tile
 constexpr int kRouterGemmMinT = 64;  // tokens from which the router uses MFMA
 
+// expert GEMM modes (values shared with the grouped GEMM kernel's modes)
+constexpr int kGemmGateUp = 2;
+constexpr int kGemmDown = 4;
+
 struct GemmArgs {
   int T, K, S, E, H, I, r;
   float lam;
@@ -23,12 +27,16 @@ struct GemmArgs {
   const unsigned long long* gblob;  // [E+1] blob address per group
   BlobLayout L;
   // activations
-  const uint16_t* x;          // [T][H]
-  const uint16_t* hs;         // [NR][I] h (fp16) in sorted rows
-  uint16_t* hs_out;
-  const uint16_t* u;          // [NR][64] lambda * A_g x, A_u x as bf16 hi/lo pairs
+  const uint16_t* x;          // [T][H] bf16
+  const uint16_t* x16;        // [T][H] fp16 x * 2^-ex[t]
+  const int32_t* ex;          // [T]
+  float* hf;                  // [NR][I] SwiGLU output h (fp32) in sorted rows
+  uint32_t* hmax;             // [NR] float bits of max |h| per row (zeroed by the setup)
+  const uint16_t* hs;         // [NR][I] fp16 h * 2^-eh[s]
+  const int32_t* eh;          // [NR]
+  const uint16_t* u;          // [NR][64] lambda * (A_g x, A_u x) * 2^-ex as bf16 hi/lo pairs
   uint16_t* u_out;
-  const uint16_t* ud;         // [NR][64] lambda * A_d h as fp16 hi/lo pairs
+  const uint16_t* ud;         // [NR][64] lambda * (A_d h) * 2^-eh as bf16 hi/lo pairs
   uint16_t* ud_out;
   // router GEMM
   const int8_t* rq;
@@ -48,6 +56,12 @@ hipError_t launch_group(const int32_t* idx, int T, int K, int E, int32_t* counts
 hipError_t launch_router_gemm(const GemmArgs& a, hipStream_t st);
 int prefill_max_mtiles(int T, int K, int E, int S);
 hipError_t launch_prefill_experts(const GemmArgs& a, const int32_t* counts, ExpertSource src,
-                                  const uint8_t* shared_blob, hipStream_t st);
+                                  const uint8_t* shared_blob, uint16_t* x16, int32_t* ex,
+                                  uint16_t* hs16, int32_t* eh, hipStream_t st);
+// expert_gemm.hip
+hipError_t launch_x16(const uint16_t* x, int T, int H, uint16_t* x16, int32_t* ex, hipStream_t st);
+hipError_t launch_h16(const float* h, const uint32_t* hmax, const int32_t* nrows, int NR, int I,
+                      uint16_t* hs16, int32_t* eh, hipStream_t st);
+hipError_t launch_expert_gemm(int mode, const GemmArgs& a, int mtiles, hipStream_t st);
 
 }  // namespace moe

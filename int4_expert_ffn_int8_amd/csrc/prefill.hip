@@ -1,21 +1,14 @@
-// Prefill path: group (token, k) pairs by expert, then grouped MFMA GEMMs.
+// Prefill path: group (token, k) pairs by expert; router and LoRA-A GEMMs.
 //
 // [P2] "SSD 专家卸载 · Prerouter 路由预测", prefill/decode paragraph: prefill
 // loads whole layers and computes in batches, decode relies on caching and
-// prefetch.  Here prefill groups each expert's tokens and runs one dense
-// contraction per expert: int4 codes are dequantised to bf16 in LDS (affine,
-// group 64: [P3] "iPhone、Mac、Android、Windows 实测横评…", "三件套" bullets)
-// and fed to v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  The unmerged
-// LoRA delta ([P1] Recover-LoRA paragraph) is one extra 64-wide K chunk: the
-// activation side holds lambda * (A v) as a hi + lo pair (computed by a skinny
-// GEMM first), the weight side holds B twice.
-//
-// Codes enter the MFMA exactly, as the values 128 + q; the affine map of each
-// 64-column group is applied in fp32 after the MFMA: acc += s * P + (b - 128 s)
-// * (row sum of the activations over the group).  Gate/up run in bf16 (x is
-// bf16); the SwiGLU output h is stored in fp16 and the down side (LoRA-A of
-// down, down projection) runs fp16 MFMA: rounding h to bf16 would cost up to
-// 1% of the output's RMS through the down projection's cancellation.
+// prefetch.  Here prefill groups each expert's tokens (stable, by expert) and
+// runs one dense contraction per expert (the expert GEMMs are in
+// expert_gemm.hip).  This file holds the grouping kernels, the expert-GEMM
+// setup, and k_gemm for the router GEMM (int8 codes exact in bf16, fp32
+// scale per 64-column chunk) and the two skinny LoRA-A GEMMs of the unmerged
+// delta ([P1] Recover-LoRA paragraph), whose outputs lambda * (A v) are
+// stored as bf16 hi + lo pairs in the row-scaled domain of the expert GEMMs.
 //
 // Row space of the expert GEMMs ("sorted rows"): s in [0, T*K) are the routed
 // pairs in perm order (expert by expert, ascending pair id), s in [T*K,
@@ -144,9 +137,11 @@ __global__ void __launch_bounds__(1024) k_prefill_setup(const int32_t* __restric
                                                          const uint8_t* shared_blob,
                                                          int32_t* __restrict__ gstart,
                                                          int32_t* __restrict__ tstart,
-                                                         unsigned long long* __restrict__ gblob) {
+                                                         unsigned long long* __restrict__ gblob,
+                                                         uint32_t* __restrict__ hmax, int NR) {
   __shared__ int lds16[16];
   const int e = threadIdx.x;
+  for (int i = e; i < NR; i += 1024) hmax[i] = 0u;  // row maxima of the gate/up epilogue
   const int n = (e < E) ? counts[e] : 0;
   const int tiles = (n + kPrefillBM - 1) / kPrefillBM;
   int total;
@@ -228,8 +223,10 @@ __device__ __forceinline__ void int8x16_to_bf16(const uint4 q, uint4& lo, uint4&
 
 template <int MODE, int BM, int BN, int WM, int WN>
 __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
+  static_assert(MODE == kRouter || MODE == kLoraGU || MODE == kLoraD,
+                "k_gemm: router and LoRA-A GEMMs (the expert GEMMs are k_expert_gemm)");
   using C = TileCfg<BM, BN, WM, WN>;
-  constexpr bool kF16 = (MODE == kLoraD || MODE == kDown);  // fp16 operands
+  constexpr bool kF16 = (MODE == kLoraD);  // fp16 operands (h * 2^-eh and A_down)
   __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDS_STRIDE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -239,9 +236,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   int ntn, Kdim, Nrows;
   if (MODE == kRouter) { Kdim = a.H; Nrows = a.E + a.S; }
   else if (MODE == kLoraGU) { Kdim = a.H; Nrows = 64; }
-  else if (MODE == kGateUp) { Kdim = a.H; Nrows = 2 * a.I; }
-  else if (MODE == kLoraD) { Kdim = a.I; Nrows = 64; }
-  else { Kdim = a.I; Nrows = a.H; }
+  else { Kdim = a.I; Nrows = 64; }
   ntn = (Nrows + BN - 1) / BN;
   const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
   const int n0 = nt * BN;
@@ -271,13 +266,11 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
     const int s = row0 + m;
     if (s >= row_end) { arow[i] = nullptr; continue; }
     if (MODE == kRouter) arow[i] = a.x + size_t(s) * a.H;
-    else if (MODE == kLoraGU || MODE == kGateUp) arow[i] = a.x + size_t(token_of(a, s)) * a.H;
+    else if (MODE == kLoraGU) arow[i] = a.x + size_t(token_of(a, s)) * a.H;
     else arow[i] = a.hs + size_t(s) * a.I;
   }
 
   const int nchunks = Kdim / BK;
-  const bool lora_chunk = (MODE == kGateUp || MODE == kDown) && a.r > 0;
-  const int total_chunks = nchunks + (lora_chunk ? 1 : 0);
 
   f32x4_t acc[C::MB][C::NB];
 #pragma unroll
@@ -288,68 +281,17 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   // register staging of one chunk
   uint4 ra[C::A_SEGS];
   // B staging: int4 -> 16B codes + scale/bias; int8 -> 16B codes; bf16 -> 16B
-  constexpr int B_SEGS_INT4 = (BN * 2 + 255) / 256;   // 16B = 32 codes = half a row-chunk
   constexpr int B_SEGS_INT8 = (BN * 4 + 255) / 256;   // 16B = 16 codes
   constexpr int B_SEGS_BF16 = (BN * 8 + 255) / 256;   // 16B = 8 bf16
-  constexpr int B_SEGS = (MODE == kRouter) ? B_SEGS_INT8
-                         : (MODE == kLoraGU || MODE == kLoraD) ? B_SEGS_BF16 : B_SEGS_INT4;
-  uint4 rb[B_SEGS > B_SEGS_BF16 ? B_SEGS : B_SEGS_BF16];
-  uint32_t rsb[B_SEGS];
+  constexpr int B_SEGS = (MODE == kRouter) ? B_SEGS_INT8 : B_SEGS_BF16;
+  uint4 rb[B_SEGS];
 
   auto load_chunk = [&](int c) {
-    const bool is_lora = lora_chunk && c == nchunks;
     const int k0 = c * BK;
-    // A side
 #pragma unroll
     for (int i = 0; i < C::A_SEGS; ++i) {
-      const int m = (tid + 256 * i) >> 3;
       const uint16_t* src = arow[i];
-      if (is_lora) {
-        src = nullptr;
-        const int s = row0 + m;
-        if (s < row_end) src = (MODE == kGateUp ? a.u : a.ud) + size_t(s) * kLoraK;
-        ra[i] = src ? *reinterpret_cast<const uint4*>(src + 8 * aseg[i]) : make_uint4(0, 0, 0, 0);
-      } else {
-        ra[i] = src ? *reinterpret_cast<const uint4*>(src + k0 + 8 * aseg[i]) : make_uint4(0, 0, 0, 0);
-      }
-    }
-    // B side
-    if (is_lora) {
-      // rows of B_lora [rows][r] bf16, repeated at the hi and lo positions of
-      // the activation side: gate/up k = [g_hi 0..15 | g_lo 16..31 | u_hi 32..47
-      // | u_lo 48..63], down k = [hi 0..31 | lo 32..63]
-#pragma unroll
-      for (int i = 0; i < B_SEGS_BF16; ++i) {
-        const int sidx = tid + 256 * i;
-        const int n = sidx >> 3, seg = sidx & 7;
-        uint32_t v[4] = {0, 0, 0, 0};
-        const int R = n0 + n;
-        if (n < BN && R < Nrows) {
-          const uint16_t* Bl = reinterpret_cast<const uint16_t*>(
-              blob + (MODE == kGateUp ? a.L.b_gu : a.L.b_dn));
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t pair[2] = {0u, 0u};
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int k = 8 * seg + 2 * q + h;
-              bool ok;
-              int rr;
-              if (MODE == kGateUp) {
-                ok = ((k >> 5) == ((R >> 4) & 1));  // gate rows take k < 32, up rows k >= 32
-                rr = k & 15;
-              } else {
-                ok = true;
-                rr = k & 31;
-              }
-              if (ok && rr < a.r) pair[h] = Bl[size_t(R) * a.r + rr];
-            }
-            v[q] = pair[0] | (pair[1] << 16);
-          }
-        }
-        rb[i] = make_uint4(v[0], v[1], v[2], v[3]);
-      }
-      return;
+      ra[i] = src ? *reinterpret_cast<const uint4*>(src + k0 + 8 * aseg[i]) : make_uint4(0, 0, 0, 0);
     }
     if (MODE == kRouter) {
 #pragma unroll
@@ -361,7 +303,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
         if (n < BN && R < Nrows) q = (R < a.E) ? a.rq + size_t(R) * a.H : a.sq;
         rb[i] = q ? *reinterpret_cast<const uint4*>(q + k0 + 16 * seg) : make_uint4(0, 0, 0, 0);
       }
-    } else if (MODE == kLoraGU || MODE == kLoraD) {
+    } else {
 #pragma unroll
       for (int i = 0; i < B_SEGS_BF16; ++i) {
         const int sidx = tid + 256 * i;
@@ -382,23 +324,6 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
         }
         rb[i] = src ? *reinterpret_cast<const uint4*>(src + k0 + 8 * seg) : make_uint4(0, 0, 0, 0);
       }
-    } else {
-      const size_t off_c = (MODE == kGateUp) ? a.L.gu_codes : a.L.dn_codes;
-      const size_t off_s = (MODE == kGateUp) ? a.L.gu_sb : a.L.dn_sb;
-#pragma unroll
-      for (int i = 0; i < B_SEGS_INT4; ++i) {
-        const int sidx = tid + 256 * i;
-        const int n = sidx >> 1, half = sidx & 1;
-        const int R = n0 + n;
-        if (n < BN && R < Nrows) {
-          rb[i] = *reinterpret_cast<const uint4*>(blob + off_c + size_t(R) * (Kdim / 2) + k0 / 2 +
-                                                  16 * half);
-          rsb[i] = reinterpret_cast<const uint32_t*>(blob + off_s)[size_t(R) * (Kdim / 64) + c];
-        } else {
-          rb[i] = make_uint4(0, 0, 0, 0);
-          rsb[i] = 0;
-        }
-      }
     }
   };
 
@@ -411,31 +336,18 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
     return 0.f;
   };
 
-  // Per-chunk fp32 affine terms of the post-scaled modes: column scale, column
-  // offset (b - 128 s) and the row sums of the activations over the chunk.
+  // router: fp32 scale of each output column for the current chunk (the
+  // int8 codes enter the MFMA exactly; the scale is applied per chunk)
   __shared__ __attribute__((aligned(16))) float Ssc[BN];
-  __shared__ __attribute__((aligned(16))) float Sbp[BN];
-  __shared__ __attribute__((aligned(16))) float Xs[BM];
-  constexpr bool kPost = (MODE == kRouter || MODE == kGateUp || MODE == kDown);
+  constexpr bool kPost = (MODE == kRouter);
 
   auto store_chunk = [&](int c) {
-    const bool is_lora = lora_chunk && c == nchunks;
 #pragma unroll
     for (int i = 0; i < C::A_SEGS; ++i) {
       const int sidx = tid + 256 * i;
       *reinterpret_cast<uint4*>(&As[(sidx >> 3) * LDS_STRIDE + 8 * (sidx & 7)]) = ra[i];
-      if ((MODE == kGateUp || MODE == kDown) && !is_lora) {
-        // row sum over the 64 columns of this chunk: 8 lanes hold one row
-        const uint32_t w4[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
-        float sum = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          sum += kF16 ? f16_lo(w4[k]) + f16_hi(w4[k]) : bf16_lo(w4[k]) + bf16_hi(w4[k]);
-        sum = group_sum<8>(sum);
-        if ((sidx & 7) == 0) Xs[sidx >> 3] = sum;
-      }
     }
-    if (is_lora || MODE == kLoraGU || MODE == kLoraD) {
+    if (MODE == kLoraGU || MODE == kLoraD) {
 #pragma unroll
       for (int i = 0; i < B_SEGS_BF16; ++i) {
         const int sidx = tid + 256 * i;
@@ -447,7 +359,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
           *reinterpret_cast<uint4*>(&Bs[(sidx >> 3) * LDS_STRIDE + 8 * (sidx & 7)]) = v;
         }
       }
-    } else if (MODE == kRouter) {
+    } else {
 #pragma unroll
       for (int i = 0; i < B_SEGS_INT8; ++i) {
         const int sidx = tid + 256 * i;
@@ -458,46 +370,19 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
           uint16_t* dst = &Bs[n * LDS_STRIDE + 16 * (sidx & 3)];
           *reinterpret_cast<uint4*>(dst) = lo;
           *reinterpret_cast<uint4*>(dst + 8) = hi;
-          if ((sidx & 3) == 0) {
-            Ssc[n] = router_scale(n, c);
-            Sbp[n] = 0.f;
-          }
-        }
-      }
-    } else {
-      // int4: exact codes as the bf16 values 128 + q; the affine map is applied
-      // in fp32 after the MFMA (s * P + (b - 128 s) * rowsum)
-#pragma unroll
-      for (int i = 0; i < B_SEGS_INT4; ++i) {
-        const int sidx = tid + 256 * i;
-        const int n = sidx >> 1;
-        if (n < BN) {
-          uint16_t* dst = &Bs[n * LDS_STRIDE + 32 * (sidx & 1)];
-          const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
-#pragma unroll
-          for (int d = 0; d < 4; ++d)
-            *reinterpret_cast<uint4*>(dst + 8 * d) =
-                kF16 ? make_uint4(codes_to_f16x2_biased(w[d], 0), codes_to_f16x2_biased(w[d], 1),
-                                  codes_to_f16x2_biased(w[d], 2), codes_to_f16x2_biased(w[d], 3))
-                     : make_uint4(codes_to_bf16x2_biased(w[d], 0), codes_to_bf16x2_biased(w[d], 1),
-                                  codes_to_bf16x2_biased(w[d], 2), codes_to_bf16x2_biased(w[d], 3));
-          if ((sidx & 1) == 0) {
-            const float sc = bf16_lo(rsb[i]);
-            Ssc[n] = sc;
-            Sbp[n] = fmaf(-128.0f, sc, bf16_hi(rsb[i]));
-          }
+          if ((sidx & 3) == 0) Ssc[n] = router_scale(n, c);
         }
       }
     }
   };
 
   load_chunk(0);
-  for (int c = 0; c < total_chunks; ++c) {
+  for (int c = 0; c < nchunks; ++c) {
     __syncthreads();
     store_chunk(c);
     __syncthreads();
-    if (c + 1 < total_chunks) load_chunk(c + 1);
-    const bool post = kPost && !(lora_chunk && c == nchunks);
+    if (c + 1 < nchunks) load_chunk(c + 1);
+    const bool post = kPost;
     f32x4_t part[C::MB][C::NB];
 #pragma unroll
     for (int i = 0; i < C::MB; ++i)
@@ -529,25 +414,13 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
         }
     }
     if (post) {
-      float xg[C::MB][4];
-#pragma unroll
-      for (int i = 0; i < C::MB; ++i) {
-        if (MODE == kRouter) {
-          xg[i][0] = xg[i][1] = xg[i][2] = xg[i][3] = 0.f;
-        } else {
-          const float4 v = *reinterpret_cast<const float4*>(&Xs[wm0 + 16 * i + 4 * (lane >> 4)]);
-          xg[i][0] = v.x; xg[i][1] = v.y; xg[i][2] = v.z; xg[i][3] = v.w;
-        }
-      }
 #pragma unroll
       for (int j = 0; j < C::NB; ++j) {
         const float sc = Ssc[wn0 + 16 * j + (lane & 15)];
-        const float bp = Sbp[wn0 + 16 * j + (lane & 15)];
 #pragma unroll
         for (int i = 0; i < C::MB; ++i)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            acc[i][j][q] = fmaf(sc, part[i][j][q], fmaf(bp, xg[i][q], acc[i][j][q]));
+          for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(sc, part[i][j][q], acc[i][j][q]);
       }
     } else {
 #pragma unroll
@@ -565,15 +438,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
       const int m = wm0 + 16 * i + 4 * (lane >> 4) + q;
       const int s = row0 + m;
       if (s >= row_end) continue;
-      if (MODE == kGateUp) {
-#pragma unroll
-        for (int j = 0; j < C::NB; j += 2) {
-          const int R = n0 + wn0 + 16 * j + (lane & 15);  // gate blob row
-          const int jj = ((R >> 5) << 4) | (R & 15);
-          const float hv = silu_f(acc[i][j][q]) * acc[i][j + 1][q];
-          a.hs_out[size_t(s) * a.I + jj] = f32_to_f16_sat(hv);
-        }
-      } else {
+      {
 #pragma unroll
         for (int j = 0; j < C::NB; ++j) {
           const int n = n0 + wn0 + 16 * j + (lane & 15);
@@ -582,31 +447,14 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
             if (n < a.E) a.logits[size_t(s) * a.E + n] = v + (a.bias ? a.bias[n] : 0.f);
             else if (n < Nrows) a.sg_logit[s] = v;
           } else if (MODE == kLoraGU || MODE == kLoraD) {
-            // lambda * (A v) as a hi + lo pair: bf16 for gate/up (about 16
-            // significant bits), fp16 for down (about 22)
-            const float lv = a.lam * v;
+            // lambda * (A v), in the row's scaled domain of the expert GEMM
+            // (x rows enter as x * 2^-ex[token]; the down side's A operand is
+            // already h * 2^-eh), as a bf16 hi + lo pair (about 16 significant bits)
+            const float lv = (MODE == kLoraGU) ? ldexpf(a.lam * v, -a.ex[token_of(a, s)]) : a.lam * v;
             const bool lo_col = (MODE == kLoraGU) ? (n & 16) : (n & 32);
-            uint16_t out;
-            if (kF16) {
-              const uint16_t hi = f32_to_f16_sat(lv);
-              out = lo_col ? f32_to_f16_sat(lv - f16_to_f32(hi)) : hi;
-            } else {
-              const uint16_t hi = f32_to_bf16(lv);
-              out = lo_col ? f32_to_bf16(lv - bf16_to_f32(hi)) : hi;
-            }
+            const uint16_t hi = f32_to_bf16(lv);
+            const uint16_t out = lo_col ? f32_to_bf16(lv - bf16_to_f32(hi)) : hi;
             if (n < kLoraK) (MODE == kLoraGU ? a.u_out : a.ud_out)[size_t(s) * kLoraK + n] = out;
-          } else {  // kDown
-            if (n < Nrows) {
-              const int TK = a.T * a.K, KS = a.K + a.S;
-              size_t dest;
-              if (s < TK) {
-                const int pr = a.perm[s];
-                dest = size_t(pr / a.K) * KS + pr % a.K;
-              } else {
-                dest = size_t(s - TK) * KS + a.K;
-              }
-              a.y[dest * a.H + n] = v;
-            }
           }
         }
       }
@@ -647,20 +495,25 @@ int prefill_max_mtiles(int T, int K, int E, int S) {
 }
 
 hipError_t launch_prefill_experts(const GemmArgs& a, const int32_t* counts, ExpertSource src,
-                                  const uint8_t* shared_blob, hipStream_t st) {
+                                  const uint8_t* shared_blob, uint16_t* x16, int32_t* ex,
+                                  uint16_t* hs16, int32_t* eh, hipStream_t st) {
+  const int NR = a.T * a.K + a.S * a.T;
   hipLaunchKernelGGL(k_prefill_setup, dim3(1), dim3(1024), 0, st, counts, a.offsets, a.E, a.T,
                      a.K, a.S, src, shared_blob, const_cast<int32_t*>(a.gstart),
-                     const_cast<int32_t*>(a.tstart), const_cast<unsigned long long*>(a.gblob));
+                     const_cast<int32_t*>(a.tstart), const_cast<unsigned long long*>(a.gblob),
+                     a.hmax, NR);
+  hipError_t e = launch_x16(a.x, a.T, a.H, x16, ex, st);
+  if (e != hipSuccess) return e;
   const int mt = prefill_max_mtiles(a.T, a.K, a.E, a.S);
   if (a.r > 0)
     hipLaunchKernelGGL((k_gemm<kLoraGU, kPrefillBM, 64, 2, 2>), dim3(mt), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((k_gemm<kGateUp, kPrefillBM, 128, 2, 2>), dim3(mt * ((2 * a.I + 127) / 128)),
-                     dim3(256), 0, st, a);
+  e = launch_expert_gemm(kGemmGateUp, a, mt, st);
+  if (e != hipSuccess) return e;
+  e = launch_h16(a.hf, a.hmax, a.gstart + a.E + 1, NR, a.I, hs16, eh, st);
+  if (e != hipSuccess) return e;
   if (a.r > 0)
     hipLaunchKernelGGL((k_gemm<kLoraD, kPrefillBM, 64, 2, 2>), dim3(mt), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((k_gemm<kDown, kPrefillBM, 128, 2, 2>), dim3(mt * ((a.H + 127) / 128)),
-                     dim3(256), 0, st, a);
-  return hipGetLastError();
+  return launch_expert_gemm(kGemmDown, a, mt, st);
 }
 
 }  // namespace moe

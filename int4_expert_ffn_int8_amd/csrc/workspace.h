@@ -24,8 +24,13 @@ struct WsLayout {
   size_t tstart;      // int32 [E+2]
   size_t gblob;       // u64 [E+1]
   size_t pu;          // bf16 [NR, 64]  lambda * LoRA-A of gate/up
-  size_t pud;         // fp16 [NR, 64]  lambda * LoRA-A of down (hi/lo pairs)
-  size_t phs;         // fp16 [NR, I]   h in sorted rows
+  size_t pud;         // bf16 [NR, 64]  lambda * LoRA-A of down (hi/lo pairs)
+  size_t x16;         // fp16 [T, H]    x * 2^-ex (prefill)
+  size_t ex;          // int32 [T]
+  size_t hf;          // fp32 [NR, I]   h in sorted rows
+  size_t hmax;        // u32 [NR]       max |h| per row
+  size_t hs16;        // fp16 [NR, I]   h * 2^-eh
+  size_t eh;          // int32 [NR]
   size_t total;
 };
 
@@ -52,7 +57,13 @@ inline WsLayout ws_layout(const moe_dims_t& d, int T, bool prefill) {
   W.gblob = o;      o = align256(o + (prefill ? (E + 1) * 8 : 0));
   W.pu = o;         o = align256(o + NR * kLoraK * 2);
   W.pud = o;        o = align256(o + NR * kLoraK * 2);
-  W.phs = o;        o = align256(o + NR * d.I * 2);
+  const size_t TP = prefill ? size_t(T) : 0;
+  W.x16 = o;        o = align256(o + TP * d.H * 2);
+  W.ex = o;         o = align256(o + TP * 4);
+  W.hf = o;         o = align256(o + NR * d.I * 4);
+  W.hmax = o;       o = align256(o + NR * 4);
+  W.hs16 = o;       o = align256(o + NR * d.I * 2);
+  W.eh = o;         o = align256(o + NR * 4);
   W.total = o;
   return W;
 }
