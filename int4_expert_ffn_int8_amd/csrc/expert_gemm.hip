@@ -97,8 +97,7 @@ __global__ void __launch_bounds__(256) k_h16(const float* __restrict__ h, const 
 }
 
 // ---------------------------------------------------------------------------
-constexpr int EBM = 128, EBN = 128, EBK = 64;
-constexpr int ELDS = EBK + 8;  // fp16 elements per LDS row (144 bytes)
+constexpr int EBM = 128, EBN = 256, EKC = 64;  // tile rows, tile columns, K per chunk
 
 // token of sorted row s
 __device__ __forceinline__ int etoken_of(const GemmArgs& a, int s) {
@@ -140,26 +139,99 @@ __device__ __forceinline__ bool xcd_tile(int bid, int active_mt, int ntn, int& m
   return slot / ntn < run && mt < active_mt;
 }
 
+// Buffer resource over [p, p + bytes) in scalar registers (raw buffer:
+// stride 0, 32-bit offsets); reads at or past `bytes` return zero.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  return i32x4_t{__builtin_amdgcn_readfirstlane(int32_t(uint32_t(b))),
+                 __builtin_amdgcn_readfirstlane(int32_t(uint32_t(b >> 32) & 0xFFFFu)),
+                 __builtin_amdgcn_readfirstlane(int32_t(bytes)), 0x00020000};
+}
+constexpr uint32_t kOobOffset = 0x80000000u;  // an offset past every buffer (sizes < 2^31): reads zero
+
+// 16 / 4 bytes per lane from global memory straight into LDS: lane L of the
+// wave writes lds + 16 L (resp. 4 L); completion is counted by vmcnt.  The
+// instruction is written out here (M0 saved and restored around it) because
+// the compiler's own tracking of such fetches waits for all of them before
+// any LDS read; the kernels below wait for them explicitly instead.
+__device__ __forceinline__ void dma16(i32x4_t r, const void* lds, uint32_t voff, uint32_t soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds)))), "v"(voff), "s"(r),
+        "s"(soff)
+      : "memory");
+}
+__device__ __forceinline__ void dma4(i32x4_t r, const void* lds, uint32_t voff, uint32_t soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds)))), "v"(voff), "s"(r),
+        "s"(soff)
+      : "memory");
+}
+
+// (x & mask) | magic in one VALU op (mask in a VGPR: one scalar operand)
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t vmask, uint32_t magic) {
+  uint32_t d;
+  asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(x), "v"(vmask), "s"(magic));
+  return d;
+}
+
 // Eight int4 codes of one 32-bit word (columns 2s and 2s+1 in the bits
-// [4s, 4s+4) and [16+4s, 20+4s)) -> fp16 s*q + b, two per output word.
-__device__ __forceinline__ void dequant8_f16(uint32_t w, f16x2_t sc, f16x2_t bi, uint32_t (&o)[4]) {
+// [4s, 4s+4) and [16+4s, 20+4s)) -> fp16 s*q + b, two per output word: the
+// code fills the low mantissa bits of fp16 1024 (0x6400), 1024 is subtracted
+// exactly and one fused multiply-add applies the group's scale and bias.
+__device__ __forceinline__ f16x8_t dequant8_fast(uint32_t w, uint32_t vmask, f16x2_t sc, f16x2_t bi) {
   const f16x2_t off = {_Float16(1024.0f), _Float16(1024.0f)};
+  u32x4_t o;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    // 0x6400 is fp16 1024 with a zero mantissa: the code fills the low bits
-    const uint32_t c = ((w >> (4 * s)) & 0x000F000Fu) | 0x64006400u;
+    const uint32_t c = and_or(s ? (w >> (4 * s)) : w, vmask, 0x64006400u);
     const f16x2_t q = __builtin_bit_cast(f16x2_t, c) - off;  // exact
     o[s] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, sc, bi));
   }
+  return __builtin_bit_cast(f16x8_t, o);
 }
 
+// LDS stage of the ring, one K chunk of 64 (one quantisation group):
+//   A      [128 rows][128 B]: 16-byte slot p of row r holds k-segment
+//          p ^ ((r >> 1) & 7) (8 fp16 each);
+//   codes  [256 rows][32 B]:  8-byte unit p of row r holds the 16 codes
+//          k = 16 (p ^ 2 ((r >> 3) & 1)) + 0..15;
+//   scale/bias [256 rows] words.
+// The XOR swizzles make the MFMA operand reads of every 16 lanes hit
+// distinct LDS banks.
+constexpr int kStA = 0, kStB = EBM * 128, kStS = kStB + EBN * 32, kStage = kStS + EBN * 4;
+
+// Grouped expert GEMM, one 128-row x 256-column tile per workgroup of 8
+// waves; wave w owns all 128 rows and columns 32 w .. 32 w + 31 (8 x 2
+// blocks of 16 x 16), so each weight is dequantised once per tile.  Two
+// workgroups share a CU (four waves per SIMD) to cover LDS and barrier
+// latency with the other waves' MFMAs.
 template <int MODE>
-__global__ void __launch_bounds__(256, 2) k_expert_gemm(GemmArgs a, int nblk) {
+__global__ void __launch_bounds__(512, 4) k_expert_gemm(GemmArgs a, int nblk) {
   static_assert(MODE == kGemmGateUp || MODE == kGemmDown, "expert GEMM modes");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][EBM * ELDS];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][EBN * ELDS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm0 = (wave >> 1) * 64, wn0 = (wave & 1) * 64;
+  constexpr int IM = EBM / 16;      // 16-row blocks per wave
+  constexpr int JN = EBN / 8 / 16;  // 16-column blocks per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t S0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t S1[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t S2[kStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15, lq = lane >> 4;
+  const int wn0 = wave * (EBN / 8);
 
   const int Kdim = (MODE == kGemmGateUp) ? a.H : a.I;
   const int Nrows = (MODE == kGemmGateUp) ? 2 * a.I : a.H;
@@ -173,10 +245,9 @@ __global__ void __launch_bounds__(256, 2) k_expert_gemm(GemmArgs a, int nblk) {
   const int n0 = nt * EBN;
   const uint8_t* blob = reinterpret_cast<const uint8_t*>(a.gblob[g]);
 
-  // Per-row facts of the tile, resolved once (dependent loads of perm and the
-  // exponents) into LDS: the activation row (token for gate/up), the output
-  // row of y (down) and the row exponent.  Rows past the group end are
-  // clamped to its last row: they are computed, not stored.
+  // Per-row facts of the tile, resolved once into LDS: the activation row
+  // (token for gate/up), the output row of y (down) and the row exponent.
+  // Rows past the group end are clamped to its last row: computed, not stored.
   __shared__ int row_src[EBM], row_dst[EBM], row_e[EBM];
   if (tid < EBM) {
     const int s = min(row0 + tid, row_end - 1);
@@ -198,199 +269,199 @@ __global__ void __launch_bounds__(256, 2) k_expert_gemm(GemmArgs a, int nblk) {
       row_e[tid] = a.eh[s];
     }
   }
-  __syncthreads();
-  // A: 4 segments of 8 elements per thread per chunk (row sidx>>3, seg sidx&7)
-  const uint16_t* arow[4];
+
+  __syncthreads();  // row tables
+
+  // ---- global -> LDS fetch of one K chunk: A 2 and codes 1 DMA instruction
+  // per thread, scale/bias 1 per thread of waves 0..3; each wave instruction
+  // writes 1 KB (256 B) of contiguous LDS.
+  const i32x4_t ra = buffer_rsrc(
+      (MODE == kGemmGateUp) ? (const void*)a.x16 : (const void*)a.hs,
+      uint32_t((MODE == kGemmGateUp) ? size_t(a.T) * a.H * 2 : size_t(a.gstart[G]) * a.I * 2));
+  const i32x4_t rb = buffer_rsrc(blob, uint32_t(a.L.total));
+  uint32_t aoff[2], boff, soff;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = row_src[(tid + 256 * i) >> 3];
-    arow[i] = (MODE == kGemmGateUp) ? a.x16 + size_t(r) * a.H : a.hs + size_t(r) * a.I;
+  for (int u = 0; u < 2; ++u) {  // A: LDS slot (8 u + wave) * 64 + lane
+    const int idx = (8 * u + wave) * 64 + lane, r = idx >> 3;
+    const int seg = (idx & 7) ^ ((r >> 1) & 7);
+    aoff[u] = uint32_t(row_src[r]) * uint32_t(Kdim) * 2u + 16u * seg;
   }
-  const int nchunks = Kdim / EBK;
-  const bool lora = a.r > 0;
+  {  // codes: LDS 16-byte slot wave * 64 + lane = row r, half h (units 2h, 2h + 1)
+    const int idx = wave * 64 + lane, r = idx >> 1, h = idx & 1;
+    const int R = min(n0 + r, Nrows - 1);  // columns past Nrows: computed, not stored
+    boff = uint32_t(((MODE == kGemmGateUp) ? a.L.gu_codes : a.L.dn_codes) + size_t(R) * (Kdim / 2)) +
+           16u * (h ^ ((r >> 3) & 1));
+  }
+  {  // scale/bias: LDS word wave * 64 + lane = row r (waves 0..3)
+    const int R = min(n0 + (wave & 3) * 64 + lane, Nrows - 1);
+    soff = uint32_t(((MODE == kGemmGateUp) ? a.L.gu_sb : a.L.dn_sb) + size_t(R) * (Kdim / 64) * 4);
+  }
+  const int nchunks = Kdim / EKC;
+  const int clast = nchunks - 1;
+  auto fetch = [&](uint8_t* st, int c) {
+    dma16(ra, st + kStA + wave * 1024, aoff[0], c * (EKC * 2));
+    dma16(ra, st + kStA + (8 + wave) * 1024, aoff[1], c * (EKC * 2));
+    dma16(rb, st + kStB + wave * 1024, boff, c * (EKC / 2));
+    if (wave < 4) dma4(rb, st + kStS + wave * 256, soff, c * 4);
+  };
+  // wait for this wave's fetches of the chunk before the newest one
+  auto wait_prev = [&]() {
+    if (wave < 4)
+      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F73);  // vmcnt(3)
+  };
 
-  // B: one weight row half (32 codes) per thread: row n = tid >> 1, half = tid & 1
-  const int bn = tid >> 1, bhalf = tid & 1;
-  const int R = min(n0 + bn, Nrows - 1);  // columns past Nrows are computed, not stored
-  const uint8_t* bcodes = blob + (MODE == kGemmGateUp ? a.L.gu_codes : a.L.dn_codes) +
-                          size_t(R) * (Kdim / 2) + 16 * bhalf;
-  const uint32_t* bsb = reinterpret_cast<const uint32_t*>(
-      blob + (MODE == kGemmGateUp ? a.L.gu_sb : a.L.dn_sb)) + size_t(R) * (Kdim / 64);
+  f32x4_t acc[IM][JN];
+#pragma unroll
+  for (int i = 0; i < IM; ++i)
+#pragma unroll
+    for (int j = 0; j < JN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // The LoRA chunk's operands, loaded first (used after the main loop):
-  // A = lambda * (A v) * 2^-e hi/lo pairs of the tile's rows, B = this thread's
-  // 32 k values of B row R (gate/up: k = [gate hi 0..15 | gate lo 16..31 | up
-  // hi 32..47 | up lo 48..63], a gate row (R & 16 == 0) takes k < 32, an up
-  // row k >= 32; down: k = [hi 0..31 | lo 32..63]).
-  uint4 la[4], lb[4];
-  if (lora) {
+  const uint32_t vmask = 0x000F000Fu;
+  // one chunk from stage st: 2 MFMA steps of 32 k.  Lane (ln, lq) takes the
+  // codes k = 16 lq + 0..15 of its columns, step t their codes 8 t .. 8 t + 7;
+  // the activation side reads the same k (segment 2 lq + t).
+  const int bslot = 8 * (lq ^ (2 * (ln >> 3)));
+  const int abase = ln * 128;
+  const int aswz = (ln >> 1) & 7;
+  auto compute = [&](const uint8_t* st) {
+    uint2 q[JN];
+    f16x2_t sc[JN], bi[JN];
+#pragma unroll
+    for (int j = 0; j < JN; ++j) {
+      const int r = wn0 + 16 * j + ln;
+      q[j] = *reinterpret_cast<const uint2*>(st + kStB + r * 32 + bslot);
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(st + kStS + r * 4);
+      sc[j] = f16x2_t{_Float16(bf16_lo(sw)), _Float16(bf16_lo(sw))};
+      bi[j] = f16x2_t{_Float16(bf16_hi(sw)), _Float16(bf16_hi(sw))};
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f16x8_t bf[JN];
+#pragma unroll
+      for (int j = 0; j < JN; ++j) bf[j] = dequant8_fast(t ? q[j].y : q[j].x, vmask, sc[j], bi[j]);
+      const uint8_t* as = st + kStA + abase + 16 * ((2 * lq + t) ^ aswz);
+#pragma unroll
+      for (int i = 0; i < IM; ++i) {
+        const f16x8_t af = *reinterpret_cast<const f16x8_t*>(as + i * 16 * 128);
+#pragma unroll
+        for (int j = 0; j < JN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+  // Pipeline over a ring of three LDS stages: chunk c lives in stage c % 3.
+  // Each step waits for its own fetches of chunk c (those of chunk c + 1 stay
+  // in flight), meets the other waves at the barrier (after which chunk c is
+  // complete in LDS and stage (c + 2) % 3 is no longer read), starts the
+  // fetch of chunk c + 2 into that stage and computes chunk c.  The loop body
+  // covers three chunks so each stage is a distinct array; fetch indices are
+  // clamped and a step past the end skips its MFMAs, so the body has no exit.
+  fetch(S0, 0);
+  fetch(S1, min(1, clast));
+#define MOE_STEP(CUR, NXT, I)                 \
+  wait_prev();                                \
+  __syncthreads();                            \
+  fetch(NXT, min(c + (I) + 2, clast));        \
+  if (c + (I) < nchunks) compute(CUR);
+  for (int c = 0; c < nchunks; c += 3) {
+    MOE_STEP(S0, S2, 0)
+    MOE_STEP(S1, S0, 1)
+    MOE_STEP(S2, S1, 2)
+  }
+#undef MOE_STEP
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no fetch still writes LDS
+  __syncthreads();
+
+  if (a.r > 0) {  // the LoRA chunk, in stage 0's A layout
     const uint16_t* src = (MODE == kGemmGateUp) ? a.u : a.ud;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = min(row0 + ((tid + 256 * i) >> 3), row_end - 1);
-      la[i] = gload16(src + size_t(s) * kLoraK + 8 * ((tid + 256 * i) & 7));
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 512 * i, m = idx >> 3, sg = idx & 7;
+      const int s = min(row0 + m, row_end - 1);
+      *reinterpret_cast<u32x4_t*>(S0 + kStA + m * 128 + 16 * (sg ^ ((m >> 1) & 7))) =
+          gload<u32x4_t>(src + size_t(s) * kLoraK + 8 * sg);
     }
+    __syncthreads();
+    // Weight side: B[R][rr] as bf16 for the k the lane covers.  Activation
+    // side u: gate/up k = [gate hi 0..15 | gate lo 16..31 | up hi 32..47 |
+    // up lo 48..63], so a gate column block (j even) meets step 0 only and an
+    // up block (j odd) step 1 only, with rank rr = 8 (lq & 1) + e; down
+    // k = [hi 0..31 | lo 32..63], both steps, rr = 8 lq + e.
     const uint16_t* Bl = reinterpret_cast<const uint16_t*>(
-        blob + (MODE == kGemmGateUp ? a.L.b_gu : a.L.b_dn)) + size_t(R) * a.r;
-    uint32_t bv[kMaxR];  // B[R][rr], every load issued (index clamped), selected below
+        blob + (MODE == kGemmGateUp ? a.L.b_gu : a.L.b_dn));
+    const int rr0 = (MODE == kGemmGateUp) ? 8 * (lq & 1) : 8 * lq;
+    bf16x8_t bw[JN];
 #pragma unroll
-    for (int rr = 0; rr < kMaxR; ++rr) bv[rr] = gload<uint16_t>(Bl + min(rr, a.r - 1));
-    uint32_t v[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      uint32_t pair[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int k = 32 * bhalf + 2 * q + h;  // compile-time within each bhalf
-        const bool ok = (MODE == kGemmGateUp) ? ((k >> 5) == ((R >> 4) & 1)) : true;
-        const int rr = (MODE == kGemmGateUp) ? (k & 15) : (k & 31);
-        pair[h] = (ok && rr < a.r && rr < kMaxR) ? bv[rr & (kMaxR - 1)] : 0u;
-      }
-      v[q] = pair[0] | (pair[1] << 16);
-    }
-#pragma unroll
-    for (int d = 0; d < 4; ++d) lb[d] = make_uint4(v[4 * d], v[4 * d + 1], v[4 * d + 2], v[4 * d + 3]);
-  }
-
-  // one K chunk of a thread's global data: 4 A segments, 32 codes and the
-  // group's scale/bias word; two sets (chunks are fetched two ahead)
-  struct Stage {
-    uint4 a0, a1, a2, a3, b;
-    uint32_t sb;
-  };
-  Stage st0, st1;
-  const int aoff = 8 * (tid & 7);  // (tid + 256 i) & 7 == tid & 7
-  auto load = [&](Stage& r, int c) {
-    r.a0 = gload16(arow[0] + c * EBK + aoff);
-    r.a1 = gload16(arow[1] + c * EBK + aoff);
-    r.a2 = gload16(arow[2] + c * EBK + aoff);
-    r.a3 = gload16(arow[3] + c * EBK + aoff);
-    r.b = gload16(bcodes + c * (EBK / 2));
-    r.sb = gload<uint32_t>(bsb + c);
-  };
-  // A rows of a thread's four segments: (tid >> 3) + 32 i, column 8 (tid & 7)
-  const int alds = (tid >> 3) * ELDS + aoff;
-  auto store = [&](const Stage& r, int buf) {
-    uint16_t* as = As[buf];
-    *reinterpret_cast<uint4*>(&as[alds]) = r.a0;
-    *reinterpret_cast<uint4*>(&as[alds + 32 * ELDS]) = r.a1;
-    *reinterpret_cast<uint4*>(&as[alds + 64 * ELDS]) = r.a2;
-    *reinterpret_cast<uint4*>(&as[alds + 96 * ELDS]) = r.a3;
-    uint16_t* dst = &Bs[buf][bn * ELDS + 32 * bhalf];
-    const f16x2_t sc = {_Float16(bf16_lo(r.sb)), _Float16(bf16_lo(r.sb))};
-    const f16x2_t bi = {_Float16(bf16_hi(r.sb)), _Float16(bf16_hi(r.sb))};
-    const uint32_t w[4] = {r.b.x, r.b.y, r.b.z, r.b.w};
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      uint32_t o[4];
-      dequant8_f16(w[d], sc, bi, o);
-      *reinterpret_cast<uint4*>(dst + 8 * d) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  };
-
-  f32x4_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // one 64-wide K chunk from LDS buffer `buf` (fp16, or bf16 for the LoRA chunk)
-  auto compute = [&](int buf, bool bf) {
-    const uint16_t* as = As[buf];
-    const uint16_t* bs = Bs[buf];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint4 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const uint4*>(&as[(wm0 + 16 * i + (lane & 15)) * ELDS + 32 * ks + 8 * (lane >> 4)]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const uint4*>(&bs[(wn0 + 16 * j + (lane & 15)) * ELDS + 32 * ks + 8 * (lane >> 4)]);
-      if (!bf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                __builtin_bit_cast(f16x8_t, af[i]), __builtin_bit_cast(f16x8_t, bfr[j]), acc[i][j], 0, 0, 0);
+    for (int j = 0; j < JN; ++j) {
+      const int R = min(n0 + wn0 + 16 * j + ln, Nrows - 1);
+      u32x4_t bw4;
+      if (a.r == kMaxR) {  // whole rows of 16: one 16-byte load (zero past the rank)
+        const u32x4_t v = gload<u32x4_t>(Bl + size_t(R) * kMaxR + min(rr0, kMaxR - 8));
+        bw4 = (rr0 < kMaxR) ? v : u32x4_t{0u, 0u, 0u, 0u};
       } else {
+        uint32_t v[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int e = 0; e < 8; ++e) v[e] = gload<uint16_t>(Bl + size_t(R) * a.r + min(rr0 + e, a.r - 1));
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, af[i]), __builtin_bit_cast(bf16x8_t, bfr[j]), acc[i][j], 0, 0, 0);
+        for (int e = 0; e < 8; e += 2) {
+          const uint32_t lo = (rr0 + e < a.r) ? v[e] : 0u;
+          const uint32_t hi = (rr0 + e + 1 < a.r) ? v[e + 1] : 0u;
+          bw4[e >> 1] = lo | (hi << 16);
+        }
+      }
+      bw[j] = __builtin_bit_cast(bf16x8_t, bw4);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint8_t* as = S0 + kStA + abase + 16 * ((4 * t + lq) ^ aswz);
+#pragma unroll
+      for (int i = 0; i < IM; ++i) {
+        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(as + i * 16 * 128);
+#pragma unroll
+        for (int j = 0; j < JN; ++j) {
+          if (MODE == kGemmGateUp && (j & 1) != t) continue;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bw[j], acc[i][j], 0, 0, 0);
+        }
       }
     }
-  };
-
-  // Pipeline: chunk c is computed from LDS buffer c & 1 while chunk c + 1
-  // (fetched during chunk c - 1) is dequantised into the other buffer and
-  // chunk c + 2 is fetched into the register set chunk c has freed.
-  load(st0, 0);
-  if (nchunks > 1) load(st1, 1);
-  store(st0, 0);
-  __syncthreads();
-  for (int c = 0; c < nchunks; c += 2) {
-    if (c + 2 < nchunks) load(st0, c + 2);
-    compute(0, false);
-    if (c + 1 < nchunks) store(st1, 1);
-    __syncthreads();
-    if (c + 1 >= nchunks) break;
-    if (c + 3 < nchunks) load(st1, c + 3);
-    compute(1, false);
-    if (c + 2 < nchunks) store(st0, 0);
-    __syncthreads();
-  }
-  if (lora) {  // the LoRA chunk (every buffer is free after the last barrier)
-    const int buf = 0;
-    uint16_t* as = As[buf];
-    *reinterpret_cast<uint4*>(&as[alds]) = la[0];
-    *reinterpret_cast<uint4*>(&as[alds + 32 * ELDS]) = la[1];
-    *reinterpret_cast<uint4*>(&as[alds + 64 * ELDS]) = la[2];
-    *reinterpret_cast<uint4*>(&as[alds + 96 * ELDS]) = la[3];
-    uint16_t* dst = &Bs[buf][bn * ELDS + 32 * bhalf];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) *reinterpret_cast<uint4*>(dst + 8 * d) = lb[d];
-    __syncthreads();
-    compute(buf, true);
   }
 
   // ---- epilogue: row scale 2^e, then SwiGLU (gate/up) or the y rows (down)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < IM; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int m = wm0 + 16 * i + 4 * (lane >> 4) + q;
+      const int m = 16 * i + 4 * lq + q;
       const int s = row0 + m;
       const bool valid = s < row_end;
       const int e = row_e[m];
       if (MODE == kGemmGateUp) {
         float hm = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; j += 2) {
-          const int Rg = n0 + wn0 + 16 * j + (lane & 15);  // gate blob row
+        for (int j = 0; j < JN; j += 2) {
+          const int Rg = n0 + wn0 + 16 * j + ln;  // gate blob row
           const int jj = ((Rg >> 5) << 4) | (Rg & 15);
-          const float g = ldexpf(acc[i][j][q], e);
+          const float gv = ldexpf(acc[i][j][q], e);
           // SiLU with the hardware exp and reciprocal (about 1e-6 relative);
           // g -> -inf gives g * 0 = -0
-          const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * ldexpf(acc[i][j + 1][q], e);
-          if (valid) a.hf[size_t(s) * a.I + jj] = hv;
-          hm = fmaxf(hm, fabsf(hv));
+          const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * ldexpf(acc[i][j + 1][q], e);
+          if (valid && Rg < Nrows) a.hf[size_t(s) * a.I + jj] = hv;
+          if (Rg < Nrows) hm = fmaxf(hm, fabsf(hv));
         }
         // the 16 lanes of one row group hold the same row: one atomic per row
         hm = fmaxf(hm, dpp_f<kDppXor1>(hm));
         hm = fmaxf(hm, dpp_f<kDppXor2>(hm));
         hm = fmaxf(hm, dpp_f<kDppHalfMirror>(hm));
         hm = fmaxf(hm, dpp_f<kDppMirror>(hm));
-        if (valid && (lane & 15) == 0) atomicMax(&a.hmax[s], __float_as_uint(hm));
+        if (valid && ln == 0) atomicMax(&a.hmax[s], __float_as_uint(hm));
       } else {
         const size_t dest = size_t(row_dst[m]);
         if (valid) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = n0 + wn0 + 16 * j + (lane & 15);
+          for (int j = 0; j < JN; ++j) {
+            const int n = n0 + wn0 + 16 * j + ln;
             if (n < Nrows) a.y[dest * a.H + n] = ldexpf(acc[i][j][q], e);
           }
         }
@@ -420,10 +491,14 @@ hipError_t launch_expert_gemm(int mode, const GemmArgs& a, int mtiles, hipStream
   const int nrows = (mode == kGemmGateUp) ? 2 * a.I : a.H;
   const int nblk = expert_gemm_blocks(mtiles, nrows);
   if (nblk <= 0) return hipSuccess;
+  // buffer offsets are 32-bit: activations, weights of one expert
+  const size_t NR = size_t(a.T) * (a.K + a.S);
+  if (size_t(a.T) * a.H * 2 > 0x7FFFFFFFu || NR * a.I * 2 > 0x7FFFFFFFu || a.L.total > 0x7FFFFFFFu)
+    return hipErrorInvalidValue;
   if (mode == kGemmGateUp)
-    hipLaunchKernelGGL(k_expert_gemm<kGemmGateUp>, dim3(nblk), dim3(256), 0, st, a, nblk);
+    hipLaunchKernelGGL(k_expert_gemm<kGemmGateUp>, dim3(nblk), dim3(512), 0, st, a, nblk);
   else
-    hipLaunchKernelGGL(k_expert_gemm<kGemmDown>, dim3(nblk), dim3(256), 0, st, a, nblk);
+    hipLaunchKernelGGL(k_expert_gemm<kGemmDown>, dim3(nblk), dim3(512), 0, st, a, nblk);
   return hipGetLastError();
 }
 

@@ -101,6 +101,15 @@ def test_prefill_equals_decode_path():
     assert_close_rms(yp, yd, "prefill vs decode y")
 
 
+@pytest.mark.parametrize("H,I", [(256, 64), (64, 128)])
+def test_prefill_k_not_multiple_of_128(H, I):
+    # the expert GEMMs take K in chunks of 128: a last chunk of 64 is padded
+    # with zero activations and zero weights
+    w = synth.workload(0, H=H, I=I)
+    L, router, experts, shared = _layer(w, seed=11)
+    _run_prefill(w, L, router, experts, shared, synth.tokens(w, 3, T=90, seed=11), max_near_ties=2)
+
+
 def test_prefill_no_shared_k8_no_lora():
     w = synth.workload(2, r=0)
     L, router, experts, shared = _layer(w)
