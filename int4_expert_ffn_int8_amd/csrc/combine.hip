@@ -19,8 +19,9 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// grid T, block 256.  Each thread walks columns tid, tid+256, ... so loads are
-// coalesced; the expert order of the sum is fixed (k = 0..K-1, then shared).
+// grid T, block 256.  Each thread takes 8 consecutive columns (two 16-byte
+// loads per expert row, issued four rows at a time); the expert order of the
+// sum is fixed (k = 0..K-1, then shared).
 __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y,
                                                   const float* __restrict__ w,
                                                   const float* __restrict__ sw, int K, int S, int H,
@@ -30,27 +31,61 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y,
   __shared__ float red[4];
   const int t = blockIdx.x;
   const int KS = K + S;
-  float wk[kMaxK + 1];
-#pragma unroll
-  for (int k = 0; k < kMaxK; ++k) wk[k] = (k < K) ? w[size_t(t) * K + k] : 0.f;
   const float g = S ? sw[t] : 0.f;
   const float* yt = y + size_t(t) * KS * H;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < H; i += 256) {
-    float o = 0.f;
-    for (int k = 0; k < K; ++k) o = fmaf(wk[k], yt[size_t(k) * H + i], o);
-    if (S) o = fmaf(g, yt[size_t(K) * H + i], o);
-    if (residual) o += bf16_to_f32(residual[size_t(t) * H + i]);
-    const uint16_t ob = f32_to_bf16(o);
-    out[size_t(t) * H + i] = ob;
-    const float ov = bf16_to_f32(ob);
-    ss = fmaf(ov, ov, ss);
+  for (int c = threadIdx.x; c < H / 8; c += 256) {
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < KS; k0 += 4) {
+      float4 v[4][2];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {  // rows past KS re-read the last row (not summed)
+        const float4* src = reinterpret_cast<const float4*>(yt + size_t(min(k0 + u, KS - 1)) * H) + 2 * c;
+        v[u][0] = src[0];
+        v[u][1] = src[1];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = k0 + u;
+        if (k >= KS) break;
+        const float coef = (k < K) ? w[size_t(t) * K + k] : g;
+        const float e[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w, v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = fmaf(coef, e[i], o[i]);
+      }
+    }
+    if (residual) {
+      const uint4 rv = *reinterpret_cast<const uint4*>(residual + size_t(t) * H + 8 * c);
+      const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[2 * i] += bf16_lo(rw[i]);
+        o[2 * i + 1] += bf16_hi(rw[i]);
+      }
+    }
+    uint32_t ow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t lo = f32_to_bf16(o[2 * i]), hi = f32_to_bf16(o[2 * i + 1]);
+      ow[i] = uint32_t(lo) | (uint32_t(hi) << 16);
+      const float a0 = bf16_to_f32(lo), a1 = bf16_to_f32(hi);
+      ss = fmaf(a0, a0, ss);
+      ss = fmaf(a1, a1, ss);
+    }
+    *reinterpret_cast<uint4*>(out + size_t(t) * H + 8 * c) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
   }
   if (!norm_out) return;
   const float tot = block_sum_256(ss, red);
   const float inv = 1.0f / sqrtf(tot / float(H) + eps);
-  for (int i = threadIdx.x; i < H; i += 256)
-    norm_out[size_t(t) * H + i] = f32_to_bf16(bf16_to_f32(out[size_t(t) * H + i]) * inv);
+  for (int c = threadIdx.x; c < H / 8; c += 256) {  // the columns this thread wrote
+    const uint4 ov = *reinterpret_cast<const uint4*>(out + size_t(t) * H + 8 * c);
+    const uint32_t iw[4] = {ov.x, ov.y, ov.z, ov.w};
+    uint32_t nw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      nw[i] = uint32_t(f32_to_bf16(bf16_lo(iw[i]) * inv)) | (uint32_t(f32_to_bf16(bf16_hi(iw[i]) * inv)) << 16);
+    *reinterpret_cast<uint4*>(norm_out + size_t(t) * H + 8 * c) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
+  }
 }
 
 // grid T, block 256

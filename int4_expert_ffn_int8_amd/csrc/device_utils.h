@@ -159,4 +159,16 @@ __device__ __forceinline__ int h_block_exp(float m) {
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// Load through a global-address-space pointer (addresses read from memory
+// would otherwise be flat).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ T gload(const void* p) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) T*>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ __forceinline__ uint4 gload16(const void* p) {
+  const u32x4_t v = gload<u32x4_t>(p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 }  // namespace moe

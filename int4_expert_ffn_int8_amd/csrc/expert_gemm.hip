@@ -114,17 +114,6 @@ __device__ __forceinline__ int egroup_of_tile(const int32_t* tstart, int G, int 
   return lo;
 }
 
-// Load through a global-address-space pointer (addresses read from memory
-// would otherwise be flat).
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-template <typename T>
-__device__ __forceinline__ T gload(const void* p) {
-  return *reinterpret_cast<const __attribute__((address_space(1))) T*>(reinterpret_cast<uintptr_t>(p));
-}
-__device__ __forceinline__ uint4 gload16(const void* p) {
-  const u32x4_t v = gload<u32x4_t>(p);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
 
 // Workgroups are dispatched to the 8 XCDs round-robin (XCD = id % 8).  Each
 // XCD takes a contiguous run of the active row tiles (a run of experts, so an

@@ -322,7 +322,9 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
             src = reinterpret_cast<const uint16_t*>(blob + a.L.a_dn) + size_t(n & 31) * a.I;
           }
         }
-        rb[i] = src ? *reinterpret_cast<const uint4*>(src + k0 + 8 * seg) : make_uint4(0, 0, 0, 0);
+        // (through the global address space: src comes from a blob address
+        // read from memory and would otherwise load through flat instructions)
+        rb[i] = src ? gload16(src + k0 + 8 * seg) : make_uint4(0, 0, 0, 0);
       }
     }
   };
