@@ -238,7 +238,11 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   else if (MODE == kLoraGU) { Kdim = a.H; Nrows = 64; }
   else { Kdim = a.I; Nrows = 64; }
   ntn = (Nrows + BN - 1) / BN;
-  const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  // LoRA-A tiles may be narrower than the 128-row group tiles: each group
+  // tile then takes kPrefillBM / BM consecutive workgroups
+  constexpr int kSub = (MODE == kRouter) ? 1 : kPrefillBM / BM;
+  static_assert(MODE == kRouter || kPrefillBM % BM == 0, "LoRA-A tiles divide the group tiles");
+  const int mt = blockIdx.x / ntn / kSub, nt = blockIdx.x % ntn, sub = (blockIdx.x / ntn) % kSub;
   const int n0 = nt * BN;
   int row0, row_end, g = 0;
   const uint8_t* blob = nullptr;
@@ -250,7 +254,8 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
     const int G = a.E + 1;
     if (mt >= a.tstart[G]) return;
     g = group_of_tile(a.tstart, G, mt);
-    row0 = a.gstart[g] + (mt - a.tstart[g]) * BM;
+    row0 = a.gstart[g] + (mt - a.tstart[g]) * kPrefillBM + sub * BM;
+    if (row0 >= a.gstart[g + 1]) return;
     row_end = min(a.gstart[g + 1], row0 + BM);
     blob = reinterpret_cast<const uint8_t*>(a.gblob[g]);
   }
@@ -483,6 +488,8 @@ hipError_t launch_group(const int32_t* idx, int T, int K, int E, int32_t* counts
   return hipGetLastError();
 }
 
+constexpr int kLoraBM = 64;  // rows per LoRA-A workgroup (two per group tile)
+
 hipError_t launch_router_gemm(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = 64, BN = 64;
   const int mtn = (a.T + BM - 1) / BM, ntn = (a.E + a.S + BN - 1) / BN;
@@ -508,13 +515,13 @@ hipError_t launch_prefill_experts(const GemmArgs& a, const int32_t* counts, Expe
   if (e != hipSuccess) return e;
   const int mt = prefill_max_mtiles(a.T, a.K, a.E, a.S);
   if (a.r > 0)
-    hipLaunchKernelGGL((k_gemm<kLoraGU, kPrefillBM, 64, 2, 2>), dim3(mt), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm<kLoraGU, kLoraBM, 64, 2, 2>), dim3(mt * (kPrefillBM / kLoraBM)), dim3(256), 0, st, a);
   e = launch_expert_gemm(kGemmGateUp, a, mt, st);
   if (e != hipSuccess) return e;
   e = launch_h16(a.hf, a.hmax, a.gstart + a.E + 1, NR, a.I, hs16, eh, st);
   if (e != hipSuccess) return e;
   if (a.r > 0)
-    hipLaunchKernelGGL((k_gemm<kLoraD, kPrefillBM, 64, 2, 2>), dim3(mt), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm<kLoraD, kLoraBM, 64, 2, 2>), dim3(mt * (kPrefillBM / kLoraBM)), dim3(256), 0, st, a);
   return launch_expert_gemm(kGemmDown, a, mt, st);
 }
 
