@@ -39,6 +39,11 @@ WORKLOADS = {
     4: dict(name="block_prefill_t3300_h2048_e256_k4_i512_zipf1.1", H=2048,
             E=256, K=4, I=512, n_shared=1, r=16, lora_scale=1.0, T=3300,
             layers=1, zipf_s=1.1),
+    # the 8B-shaped layer (as in the 24-layer stack) as a second prefill
+    # workload: 128 experts, top-8, no shared expert, same token count and bias
+    5: dict(name="block_prefill_t3300_h2048_e128_k8_i512_zipf1.1", H=2048,
+            E=128, K=8, I=512, n_shared=0, r=16, lora_scale=1.0, T=3300,
+            layers=1, zipf_s=1.1),
 }
 
 _TID = {

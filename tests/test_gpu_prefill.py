@@ -172,3 +172,19 @@ def test_prefill_3300_tokens_zipf():
     counts = r["b"]["counts"].cpu().numpy()
     print("prefill 3300: rel err %.2e, experts used %d, largest group %d, near ties %s"
           % (r["rel"], (counts > 0).sum(), counts.max(), r["near"]))
+
+
+def test_prefill_8b_shape_3300_tokens_zipf():
+    # the second prefill workload: 8B-shaped layer (128 experts, top-8, no
+    # shared expert), 3300 tokens, Zipf(1.1) rank bias; group sizes differ
+    # from the 35B-shaped case (twice the pairs over half the experts)
+    w = synth.workload(5)
+    L, router, experts, shared = _layer(w)
+    assert shared is None
+    xb = synth.tokens(w, 0)
+    bias = synth.zipf_bias(w)
+    r = _run_prefill(w, L, router, experts, shared, xb, bias=bias, max_near_ties=3)
+    counts = r["b"]["counts"].cpu().numpy()
+    assert counts.sum() == w["T"] * w["K"]
+    print("prefill 8B-shaped 3300: rel err %.2e, experts used %d, largest group %d, near ties %s"
+          % (r["rel"], (counts > 0).sum(), counts.max(), r["near"]))
