@@ -188,3 +188,48 @@ def test_prefill_8b_shape_3300_tokens_zipf():
     assert counts.sum() == w["T"] * w["K"]
     print("prefill 8B-shaped 3300: rel err %.2e, experts used %d, largest group %d, near ties %s"
           % (r["rel"], (counts > 0).sum(), counts.max(), r["near"]))
+
+
+def test_prefill_through_pool_cold_and_warm_match_resident():
+    # prefill with the routed experts behind an HBM slot pool over a pinned
+    # host master copy: cold (no expert resident: the GEMMs read the host
+    # copy) and warm (the touched experts filled into slots) give the same
+    # bits as the all-resident layer, and the lookups are counted
+    from int4_expert_ffn_int8_amd import binding as B
+    from int4_expert_ffn_int8_amd.layer import dev, pack_experts
+    w = synth.workload(0)
+    L, router, experts, shared = _layer(w, seed=21)
+    xb = synth.tokens(w, 4, T=300, seed=21)
+    x = dev(xb)
+    b0 = L.buffers(300, prefill=True)
+    L.forward(x, b0)
+    torch.cuda.synchronize()
+    y_res = b0["y"].cpu().numpy().copy()
+    out_res = b0["out"].cpu().numpy().copy()
+    counts = b0["counts"].cpu().numpy()
+    touched = np.nonzero(counts)[0].astype(np.int32)
+
+    E, nb = w["E"], B.moe_expert_blob_bytes(w["H"], w["I"], w["r"])
+    host = torch.from_numpy(pack_experts(w["H"], w["I"], w["r"], experts)).pin_memory()
+    slots = torch.empty((1, 8, nb), dtype=torch.uint8, device="cuda")
+    table = torch.empty((1, E), dtype=torch.int32, device="cuda")
+    counters = torch.zeros(2, dtype=torch.int64, device="cuda")
+    pool = B.MoePool(1, E, 8, nb, slots, table, host)
+    try:
+        ex = pool.layer(0, counters)
+        for phase in ("cold", "warm"):
+            if phase == "warm":
+                n = pool.update(touched.reshape(1, -1))
+                assert n == min(len(touched), 8)
+                pool.wait_layer(0)
+            counters.zero_()
+            b = L.buffers(300, prefill=True)
+            L.forward(x, b, routed=ex)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(b["y"].cpu().numpy(), y_res, err_msg=phase)
+            np.testing.assert_array_equal(b["out"].cpu().numpy(), out_res, err_msg=phase)
+            hits, lookups = (int(v) for v in counters.cpu().numpy())
+            assert lookups == len(touched)
+            assert hits == (0 if phase == "cold" else min(len(touched), 8))
+    finally:
+        pool.close()
