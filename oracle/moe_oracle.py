@@ -41,7 +41,7 @@ __all__ = [
     "GROUP", "bf16_to_f64", "round_bf16", "bf16_value", "dequant_int4_affine",
     "dequant_int8_sym", "router_logits", "select_topk", "topk_weights",
     "shared_gate", "silu", "sigmoid", "expert_forward", "moe_block",
-    "group_pairs", "rmsnorm", "stack_layer", "prerouter", "quantize_int4_affine",
+    "group_pairs", "rmsnorm", "stack_layer", "prerouter", "prerouter_feat", "quantize_int4_affine",
     "quantize_int8_sym",
 ]
 
@@ -314,6 +314,30 @@ def prerouter(W1_bits, W2_bits, h_bits, K: int):
     h = bf16_to_f64(h_bits)
     z = silu(h @ W1.T) @ W2.T
     pred = np.stack([select_topk(z[t], K) for t in range(z.shape[0])])
+    return pred, z
+
+
+def prerouter_feat(W1_bits, W2_bits, h_bits, prev_idx, K: int):
+    """Prerouter head with routing features: the input is h with the one-hot
+    of the experts the layer executed appended, z = W2 silu(W1 [h; onehot]).
+
+    [P1] Prerouter paragraph (the head also sees the experts already
+    executed) and [P2] Prerouter paragraph (routing features as input).
+    W1 is [D, H + E]; prev_idx [T, Kp] holds expert ids, entries outside
+    [0, E) are padding.  Returns (pred [T, K], z [T, E]).
+    """
+    W1 = bf16_to_f64(W1_bits)
+    W2 = bf16_to_f64(W2_bits)
+    h = bf16_to_f64(h_bits)
+    E = W2.shape[0]
+    T = h.shape[0]
+    onehot = np.zeros((T, E))
+    for t in range(T):
+        for e in prev_idx[t]:
+            if 0 <= e < E:
+                onehot[t, e] = 1.0
+    z = silu(np.concatenate([h, onehot], axis=1) @ W1.T) @ W2.T
+    pred = np.stack([select_topk(z[t], K) for t in range(T)])
     return pred, z
 
 

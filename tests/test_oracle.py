@@ -424,3 +424,52 @@ def test_prerouter_zero_head_and_brute_force():
         zz = [math.fsum(bfv(W2[e][d]) * a[d] for d in range(D)) for e in range(E)]
         assert np.allclose(z[t], zz, rtol=1e-12, atol=1e-15)
         assert pred[t].tolist() == sorted(range(E), key=lambda e: (-zz[e], e))[:K]
+
+
+def test_prerouter_feat_pins():
+    # Prerouter with routing features (one-hot of the executed experts
+    # appended to h): pinned by (1) reduction to the plain head when the
+    # feature columns are zero, (2) brute force with explicit sums over the
+    # h part plus the selected feature columns, (3) order and padding of the
+    # executed list not mattering, (4) a feature column that dominates z.
+    rng = np.random.default_rng(31)
+    H, D, E, K = 64, 16, 10, 3
+    W1h = synth.f32_to_bf16_bits(rng.standard_normal((D, H)) * 0.1)
+    W1f = synth.f32_to_bf16_bits(rng.standard_normal((D, E)) * 0.5)
+    W2 = synth.f32_to_bf16_bits(rng.standard_normal((E, D)) * 0.1)
+    h = synth.f32_to_bf16_bits(rng.standard_normal((2, H)))
+    prev = np.array([[1, 4, 7], [0, 9, -1]], np.int32)
+    # (1) zero feature columns: the plain head
+    W1z = np.concatenate([W1h, np.zeros_like(W1f)], axis=1)
+    pz, zz = O.prerouter_feat(W1z, W2, h, prev, K)
+    p0, z0 = O.prerouter(W1h, W2, h, K)
+    np.testing.assert_array_equal(pz, p0)
+    np.testing.assert_allclose(zz, z0, rtol=1e-13, atol=1e-15)
+    # (2) brute force
+    W1 = np.concatenate([W1h, W1f], axis=1)
+    pred, z = O.prerouter_feat(W1, W2, h, prev, K)
+    for t in range(2):
+        hv = [bfv(v) for v in h[t]]
+        sel = [e for e in prev[t] if 0 <= e < E]
+        a = [math.fsum([bfv(W1h[d][i]) * hv[i] for i in range(H)] + [bfv(W1f[d][e]) for e in sel])
+             for d in range(D)]
+        a = [v / (1 + math.exp(-v)) for v in a]
+        zb = [math.fsum(bfv(W2[e][d]) * a[d] for d in range(D)) for e in range(E)]
+        assert np.allclose(z[t], zb, rtol=1e-12, atol=1e-15)
+        assert pred[t].tolist() == sorted(range(E), key=lambda e: (-zb[e], e))[:K]
+    # (3) order and padding of the executed list do not matter
+    prev2 = np.array([[7, 1, 4, -1], [9, -5, 0, 12]], np.int32)
+    p2, z2 = O.prerouter_feat(W1, W2, h, prev2, K)
+    np.testing.assert_array_equal(p2, pred)
+    np.testing.assert_allclose(z2, z, rtol=1e-13, atol=1e-15)
+    # (4) a large weight on one feature column into a hidden unit that feeds
+    # only expert 5 makes expert 5 the first prediction for tokens that
+    # executed expert 2, and changes nothing for tokens that did not
+    W1b = W1.copy()
+    W1b[0, :] = 0
+    W1b[0, H + 2] = synth.f32_to_bf16_bits(np.array([40.0]))[0]
+    W2b = np.zeros((E, D), np.uint16)
+    W2b[5, 0] = synth.f32_to_bf16_bits(np.array([1.0]))[0]
+    pb, zb2 = O.prerouter_feat(W1b, W2b, h, np.array([[2, 3, 4], [3, 4, 6]], np.int32), K)
+    assert pb[0, 0] == 5 and zb2[0, 5] > 39
+    assert np.all(zb2[1] == 0) and pb[1].tolist() == [0, 1, 2]
