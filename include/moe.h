@@ -251,6 +251,20 @@ MOE_API moe_status_t prerouter_predict(const uint16_t* W1, const uint16_t* W2, i
                                int32_t* pred_idx, float* pred_logits, void* ws, size_t ws_bytes,
                                void* stream);
 
+/* prerouter_predict_feat: the Prerouter head with routing features.  [P1]
+ * Prerouter paragraph (the head also sees the sequence of experts already
+ * executed) and [P2] Prerouter paragraph (routing features as input): the
+ * input is h with the one-hot of the experts the layer executed appended,
+ *   z = W2 silu(W1 [h; onehot(prev)]), pred = top-K of z ordered by (-z, index).
+ *   W1 device bf16 [D, H + E] (columns H + e weight expert e); prev_idx
+ *   device int32 [T, Kp] (ids outside [0, E) are ignored, so -1 pads);
+ *   everything else as prerouter_predict.  Supported: 0 <= Kp <= 16. */
+MOE_API moe_status_t prerouter_predict_feat(const uint16_t* W1, const uint16_t* W2, int32_t H,
+                                            int32_t D, int32_t E, int32_t K, const uint16_t* h,
+                                            const int32_t* prev_idx, int32_t Kp, int32_t T,
+                                            int32_t* pred_idx, float* pred_logits, void* ws,
+                                            size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Expert pool.  [P2] "SSD 专家卸载 · Prerouter 路由预测", expert-pool and
  * Prerouter paragraphs: a streaming pool caches recently used experts and

@@ -80,6 +80,8 @@ _SIGS = {
     "moe_pool_lru": (c_vp, [c_vp]),
     "prerouter_predict": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp,
                                   c_vp, c_vp, c_sz, c_vp]),
+    "prerouter_predict_feat": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_i32,
+                                       c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
 }
 
 # symbols the public header declares (checked by the CPU test suite)
@@ -87,7 +89,7 @@ HEADER_SYMBOLS = [
     "moe_last_error", "moe_expert_blob_bytes", "moe_pack_expert", "moe_workspace_bytes",
     "moe_route", "moe_expert_forward", "moe_combine", "moe_rmsnorm",
     "moe_block_decode_workspace_bytes", "moe_workspace_init", "moe_block_decode",
-    "prerouter_workspace_bytes", "prerouter_predict",
+    "prerouter_workspace_bytes", "prerouter_predict", "prerouter_predict_feat",
     "moe_lru_create", "moe_lru_destroy", "moe_lru_plan", "moe_lru_table", "moe_lru_stats",
     "moe_pool_create", "moe_pool_destroy", "moe_pool_layer", "moe_pool_update",
     "moe_pool_wait_layer", "moe_pool_sync", "moe_pool_lru",
@@ -210,6 +212,14 @@ def prerouter_predict(W1, W2, H, D, E, K, h, T, pred_idx, pred_logits, ws, strea
                                     ptr(pred_logits), ptr(ws),
                                     ws.numel() * ws.element_size() if ws is not None else 0,
                                     stream_ptr(stream)))
+
+
+def prerouter_predict_feat(W1, W2, H, D, E, K, h, prev_idx, Kp, T, pred_idx, pred_logits, ws,
+                           stream=None) -> None:
+    _check(load().prerouter_predict_feat(ptr(W1), ptr(W2), H, D, E, K, ptr(h), ptr(prev_idx), Kp,
+                                         T, ptr(pred_idx), ptr(pred_logits), ptr(ws),
+                                         ws.numel() * ws.element_size() if ws is not None else 0,
+                                         stream_ptr(stream)))
 
 
 def moe_block_decode_workspace_bytes(d: MoeDims, T: int) -> int:

@@ -14,4 +14,5 @@ from .gen import (  # noqa: F401
     tokens,
     zipf_bias,
     prerouter_tensors,
+    prerouter_feat_tensors,
 )

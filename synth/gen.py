@@ -48,7 +48,7 @@ WORKLOADS = {
 
 _TID = {
     "router_q": 1, "router_s": 2, "sgate_q": 3, "sgate_s": 4, "x": 5,
-    "zipf": 6, "pr_w1": 7, "pr_w2": 8,
+    "zipf": 6, "pr_w1": 7, "pr_w2": 8, "pr_w1f": 9,
 }
 _PROJ = ("gate", "up", "down")
 for _i, _p in enumerate(_PROJ):
@@ -162,3 +162,13 @@ def prerouter_tensors(w: dict, layer: int, seed: int = 0) -> dict:
         "W1": _bf16_normal(_rng(seed, wid, layer, "pr_w1"), 0.02, (D, H)),
         "W2": _bf16_normal(_rng(seed, wid, layer, "pr_w2"), 0.02, (E, D)),
     }
+
+
+def prerouter_feat_tensors(w: dict, layer: int, seed: int = 0) -> dict:
+    """Prerouter head with routing features after `layer`: W1 [D, H + E] (the
+    plain head's W1, then one N(0, 0.02) column per expert for the one-hot of
+    the executed experts), W2 [E, D]; bf16 bits."""
+    base = prerouter_tensors(w, layer, seed)
+    D, E, wid = w["prerouter_D"], w["E"], w["id"]
+    extra = _bf16_normal(_rng(seed, wid, layer, "pr_w1f"), 0.02, (D, E))
+    return {"W1": np.concatenate([base["W1"], extra], axis=1), "W2": base["W2"]}

@@ -47,3 +47,41 @@ def test_prerouter_zero_head_predicts_first_indices():
     W2 = np.zeros_like(pr["W2"])
     idx, z = _run(pr["W1"], W2, synth.tokens(w, 0, T=2), w["K"])
     assert np.all(z == 0) and idx.tolist() == [[0, 1, 2, 3]] * 2
+
+
+def test_prerouter_feat_35b_shape():
+    # routing-feature input: the one-hot of the experts the layer executed
+    # (here 4 per token, one token padded with -1) appended to h
+    from int4_expert_ffn_int8_amd import binding as B
+    from int4_expert_ffn_int8_amd.layer import dev
+    w = synth.workload(3)
+    pr = synth.prerouter_feat_tensors(w, 7)
+    h = synth.tokens(w, 5, T=4)
+    prev = np.array([[3, 17, 200, 255], [0, 1, 2, 3], [128, 64, 32, -1], [255, 254, 9, 100]],
+                    np.int32)
+    D, E, H, K, T = w["prerouter_D"], w["E"], w["H"], w["K"], 4
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    z = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ws = torch.empty((B.prerouter_workspace_bytes(D, E, T),), dtype=torch.uint8, device="cuda")
+    B.prerouter_predict_feat(dev(pr["W1"]), dev(pr["W2"]), H, D, E, K, dev(h), dev(prev), 4, T,
+                             idx, z, ws)
+    torch.cuda.synchronize()
+    idx, z = idx.cpu().numpy(), z.cpu().numpy()
+    pred, z_ref = O.prerouter_feat(pr["W1"], pr["W2"], h, prev, K)
+    assert_close_rms(z, z_ref, "prerouter (features) logits")
+    err = float(np.abs(z - z_ref).max())
+    for t in range(T):
+        assert O.select_topk(z[t], K).tolist() == idx[t].tolist()
+        order = np.lexsort((np.arange(E), -z_ref[t]))
+        if z_ref[t, order[K - 1]] - z_ref[t, order[K]] > 2 * err:
+            assert order[:K].tolist() == idx[t].tolist()
+    # with an empty executed list the head equals the plain one on W1's h part
+    idx0 = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    z0 = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    B.prerouter_predict_feat(dev(pr["W1"]), dev(pr["W2"]), H, D, E, K, dev(h), None, 0, T,
+                             idx0, z0, ws)
+    plain = synth.prerouter_tensors(w, 7)
+    idx1, z1 = _run(plain["W1"], plain["W2"], h, K)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(z0.cpu().numpy(), z1)
+    np.testing.assert_array_equal(idx0.cpu().numpy(), idx1)
