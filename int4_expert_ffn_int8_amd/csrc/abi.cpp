@@ -92,6 +92,7 @@ extern "C" moe_status_t moe_route(const moe_dims_t* d, const int8_t* gate_q, con
     g.bias = logit_bias;
     g.logits = lg;
     g.sg_logit = sg;
+    g.plog = reinterpret_cast<float*>(wsb + W.plog);
     st = hip_status(launch_router_gemm(g, s), fn);
   } else {
     st = hip_status(launch_router_logits(d->H, gate_q, gate_s, sgate_q, sgate_s, x, logit_bias,

@@ -11,6 +11,7 @@ namespace moe {
 constexpr int kGroupChunk = 1024;  // pairs per grouping workgroup
 constexpr int kPrefillBM = 128;    // rows (pairs/tokens) per expert-GEMM tile
 constexpr int kRouterGemmMinT = 64;  // tokens from which the router uses MFMA
+constexpr int kRouterSplit = 4;      // K splits of the router GEMM
 
 // expert GEMM modes (values shared with the grouped GEMM kernel's modes)
 constexpr int kGemmGateUp = 2;
@@ -46,6 +47,7 @@ struct GemmArgs {
   const float* bias;
   float* logits;
   float* sg_logit;
+  float* plog;  // [kRouterSplit][T][E + S] partial logits of the K splits, or null (no split)
   // down output, [T][K+S][H]
   float* y;
 };

@@ -383,12 +383,15 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
     }
   };
 
-  load_chunk(0);
-  for (int c = 0; c < nchunks; ++c) {
+  // router: split-K over blockIdx.y (partial sums of disjoint chunk ranges)
+  const int ks = blockIdx.y, nks = gridDim.y;
+  const int c0 = ks * nchunks / nks, c1 = (ks + 1) * nchunks / nks;
+  load_chunk(c0);
+  for (int c = c0; c < c1; ++c) {
     __syncthreads();
     store_chunk(c);
     __syncthreads();
-    if (c + 1 < nchunks) load_chunk(c + 1);
+    if (c + 1 < c1) load_chunk(c + 1);
     const bool post = kPost;
     f32x4_t part[C::MB][C::NB];
 #pragma unroll
@@ -451,8 +454,13 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
           const int n = n0 + wn0 + 16 * j + (lane & 15);
           const float v = acc[i][j][q];
           if (MODE == kRouter) {
-            if (n < a.E) a.logits[size_t(s) * a.E + n] = v + (a.bias ? a.bias[n] : 0.f);
-            else if (n < Nrows) a.sg_logit[s] = v;
+            if (a.plog) {  // partial of this K split; summed (and biased) by k_router_reduce
+              if (n < Nrows) a.plog[(size_t(ks) * a.T + s) * Nrows + n] = v;
+            } else if (n < a.E) {
+              a.logits[size_t(s) * a.E + n] = v + (a.bias ? a.bias[n] : 0.f);
+            } else if (n < Nrows) {
+              a.sg_logit[s] = v;
+            }
           } else if (MODE == kLoraGU || MODE == kLoraD) {
             // lambda * (A v), in the row's scaled domain of the expert GEMM
             // (x rows enter as x * 2^-ex[token]; the down side's A operand is
@@ -490,10 +498,34 @@ hipError_t launch_group(const int32_t* idx, int T, int K, int E, int32_t* counts
 
 constexpr int kLoraBM = 64;  // rows per LoRA-A workgroup (two per group tile)
 
+// logits[t][e] = sum over the K splits (in split order) + bias[e]; column E
+// (the shared-gate logit) goes to sg_logit.  grid ceil(T * (E + S) / 256).
+__global__ void __launch_bounds__(256) k_router_reduce(const float* __restrict__ plog, int nks, int T,
+                                                       int E, int S, const float* __restrict__ bias,
+                                                       float* __restrict__ logits,
+                                                       float* __restrict__ sg_logit) {
+  const int N = E + S;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * N) return;
+  const int t = i / N, n = i % N;
+  float v = 0.f;
+  for (int k = 0; k < nks; ++k) v += plog[(size_t(k) * T + t) * N + n];
+  if (n < E) logits[size_t(t) * E + n] = v + (bias ? bias[n] : 0.f);
+  else sg_logit[t] = v;
+}
+
 hipError_t launch_router_gemm(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = 64, BN = 64;
   const int mtn = (a.T + BM - 1) / BM, ntn = (a.E + a.S + BN - 1) / BN;
-  hipLaunchKernelGGL((k_gemm<kRouter, BM, BN, 2, 2>), dim3(mtn * ntn), dim3(256), 0, st, a);
+  // split K so a few thousand tokens give about 1000 workgroups with short
+  // chunk loops; the partial sums are reduced in a fixed order
+  const int nks = a.plog ? kRouterSplit : 1;
+  hipLaunchKernelGGL((k_gemm<kRouter, BM, BN, 2, 2>), dim3(mtn * ntn, nks), dim3(256), 0, st, a);
+  if (a.plog) {
+    const int n = a.T * (a.E + a.S);
+    hipLaunchKernelGGL(k_router_reduce, dim3((n + 255) / 256), dim3(256), 0, st, a.plog, nks, a.T,
+                       a.E, a.S, a.bias, a.logits, a.sg_logit);
+  }
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ struct WsLayout {
   // routing
   size_t logits;   // fp32 [T, E] (used when the caller passes no logits buffer)
   size_t sg;       // fp32 [T]    shared-gate logits
+  size_t plog;     // fp32 [kRouterSplit, T, E + S] router GEMM partials (T >= kRouterGemmMinT)
   // decode expert path
   size_t blobptr;  // u64 [NP]    resolved blob address per (token, slot)
   size_t u;        // fp32 [NP, 2r]
@@ -42,6 +43,7 @@ inline WsLayout ws_layout(const moe_dims_t& d, int T, bool prefill) {
   size_t o = 0;
   W.logits = o;  o = align256(o + size_t(T) * d.E * 4);
   W.sg = o;      o = align256(o + size_t(T) * 4);
+  W.plog = o;    o = align256(o + (T >= kRouterGemmMinT ? size_t(kRouterSplit) * T * (d.E + d.n_shared) * 4 : 0));
   W.blobptr = o; o = align256(o + NP * 8);
   W.u = o;       o = align256(o + NP * 2 * d.r * 4);
   W.h = o;       o = align256(o + NP * d.I * 4);
