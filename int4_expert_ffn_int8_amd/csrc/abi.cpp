@@ -173,6 +173,7 @@ extern "C" moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_expert
     g.eh = eh;
     g.u = g.u_out = reinterpret_cast<uint16_t*>(wsb + W.pu);
     g.ud = g.ud_out = reinterpret_cast<uint16_t*>(wsb + W.pud);
+    g.upart = reinterpret_cast<float*>(wsb + W.upart);
     g.y = y;
     return hip_status(launch_prefill_experts(g, counts, src,
                                              static_cast<const uint8_t*>(shared_blob), x16, ex,

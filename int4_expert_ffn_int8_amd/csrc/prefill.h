@@ -12,6 +12,7 @@ constexpr int kGroupChunk = 1024;  // pairs per grouping workgroup
 constexpr int kPrefillBM = 128;    // rows (pairs/tokens) per expert-GEMM tile
 constexpr int kRouterGemmMinT = 64;  // tokens from which the router uses MFMA
 constexpr int kRouterSplit = 4;      // K splits of the router GEMM
+constexpr int kLoraSplit = 4;        // K splits of the gate/up LoRA-A GEMM
 
 // expert GEMM modes (values shared with the grouped GEMM kernel's modes)
 constexpr int kGemmGateUp = 2;
@@ -48,6 +49,7 @@ struct GemmArgs {
   float* logits;
   float* sg_logit;
   float* plog;  // [kRouterSplit][T][E + S] partial logits of the K splits, or null (no split)
+  float* upart;  // [kLoraSplit][NR][32] partial LoRA-A of gate/up over the K splits
   // down output, [T][K+S][H]
   float* y;
 };

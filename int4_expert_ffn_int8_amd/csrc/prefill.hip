@@ -235,7 +235,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   // ---- which tile ---------------------------------------------------------
   int ntn, Kdim, Nrows;
   if (MODE == kRouter) { Kdim = a.H; Nrows = a.E + a.S; }
-  else if (MODE == kLoraGU) { Kdim = a.H; Nrows = 64; }
+  else if (MODE == kLoraGU) { Kdim = a.H; Nrows = 32; }  // A_gate rows 0..15, A_up rows 16..31
   else { Kdim = a.I; Nrows = 64; }
   ntn = (Nrows + BN - 1) / BN;
   // LoRA-A tiles may be narrower than the 128-row group tiles: each group
@@ -315,14 +315,15 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
         const int n = sidx >> 3, seg = sidx & 7;
         const uint16_t* src = nullptr;
         if (n < BN) {
-          // output column n computes row (n & 15) of A_gate (n < 32) or A_up
-          // (n >= 32) for gate/up, row (n & 31) of A_down for down; each row
-          // appears twice so the epilogue can store a hi and a lo bf16 part
+          // gate/up: output column n computes row (n & 15) of A_gate (n < 16)
+          // or A_up (n >= 16), summed over K splits and split into hi/lo
+          // bf16 parts by k_lora_reduce; down: row (n & 31) of A_down, each
+          // row appearing twice so the epilogue can store a hi and a lo part
           if (MODE == kLoraGU) {
             const int rr = n & 15;
             if (rr < a.r)
               src = reinterpret_cast<const uint16_t*>(blob + a.L.a_gu) +
-                    (size_t(n >= 32 ? a.r : 0) + rr) * a.H;
+                    (size_t(n >= 16 ? a.r : 0) + rr) * a.H;
           } else if ((n & 31) < a.r) {
             src = reinterpret_cast<const uint16_t*>(blob + a.L.a_dn) + size_t(n & 31) * a.I;
           }
@@ -461,15 +462,17 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
             } else if (n < Nrows) {
               a.sg_logit[s] = v;
             }
-          } else if (MODE == kLoraGU || MODE == kLoraD) {
+          } else if (MODE == kLoraGU) {  // partial of this K split
+            if (n < Nrows) a.upart[(size_t(ks) * a.gstart[a.E + 1] + s) * Nrows + n] = v;
+          } else if (MODE == kLoraD) {
             // lambda * (A v), in the row's scaled domain of the expert GEMM
             // (x rows enter as x * 2^-ex[token]; the down side's A operand is
             // already h * 2^-eh), as a bf16 hi + lo pair (about 16 significant bits)
-            const float lv = (MODE == kLoraGU) ? ldexpf(a.lam * v, -a.ex[token_of(a, s)]) : a.lam * v;
-            const bool lo_col = (MODE == kLoraGU) ? (n & 16) : (n & 32);
+            const float lv = a.lam * v;
+            const bool lo_col = n & 32;
             const uint16_t hi = f32_to_bf16(lv);
             const uint16_t out = lo_col ? f32_to_bf16(lv - bf16_to_f32(hi)) : hi;
-            if (n < kLoraK) (MODE == kLoraGU ? a.u_out : a.ud_out)[size_t(s) * kLoraK + n] = out;
+            if (n < kLoraK) a.ud_out[size_t(s) * kLoraK + n] = out;
           }
         }
       }
@@ -514,6 +517,26 @@ __global__ void __launch_bounds__(256) k_router_reduce(const float* __restrict__
   else sg_logit[t] = v;
 }
 
+// u[s] of the gate/up LoRA chunk from the K-split partials of A_gate x and
+// A_up x (columns 0..15 and 16..31): lambda * (A v) * 2^-ex[token], as
+// [gate hi 0..15 | gate lo 16..31 | up hi 32..47 | up lo 48..63] bf16, ranks
+// past r zero.  grid ceil(NR * 32 / 256).
+__global__ void __launch_bounds__(256) k_lora_reduce(GemmArgs a, int nks) {
+  const int NR = a.gstart[a.E + 1];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= NR * 32) return;
+  const int s = i >> 5, j = i & 31;
+  float v = 0.f;
+  for (int k = 0; k < nks; ++k) v += a.upart[(size_t(k) * NR + s) * 32 + j];
+  const int rr = j & 15;
+  const float lv = (rr < a.r) ? ldexpf(a.lam * v, -a.ex[token_of(a, s)]) : 0.f;
+  const uint16_t hi = f32_to_bf16(lv);
+  const uint16_t lo = f32_to_bf16(lv - bf16_to_f32(hi));
+  uint16_t* d = a.u_out + size_t(s) * kLoraK + (j >= 16 ? 32 : 0) + rr;
+  d[0] = hi;
+  d[16] = lo;
+}
+
 hipError_t launch_router_gemm(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = 64, BN = 64;
   const int mtn = (a.T + BM - 1) / BM, ntn = (a.E + a.S + BN - 1) / BN;
@@ -546,8 +569,11 @@ hipError_t launch_prefill_experts(const GemmArgs& a, const int32_t* counts, Expe
   hipError_t e = launch_x16(a.x, a.T, a.H, x16, ex, st);
   if (e != hipSuccess) return e;
   const int mt = prefill_max_mtiles(a.T, a.K, a.E, a.S);
-  if (a.r > 0)
-    hipLaunchKernelGGL((k_gemm<kLoraGU, kLoraBM, 64, 2, 2>), dim3(mt * (kPrefillBM / kLoraBM)), dim3(256), 0, st, a);
+  if (a.r > 0) {  // LoRA-A of gate/up: K split in kLoraSplit, partials summed in order
+    hipLaunchKernelGGL((k_gemm<kLoraGU, kLoraBM, 32, 2, 2>), dim3(mt * (kPrefillBM / kLoraBM), kLoraSplit),
+                       dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_lora_reduce, dim3((NR * 32 + 255) / 256), dim3(256), 0, st, a, kLoraSplit);
+  }
   e = launch_expert_gemm(kGemmGateUp, a, mt, st);
   if (e != hipSuccess) return e;
   e = launch_h16(a.hf, a.hmax, a.gstart + a.E + 1, NR, a.I, hs16, eh, st);

@@ -26,6 +26,7 @@ struct WsLayout {
   size_t gblob;       // u64 [E+1]
   size_t pu;          // bf16 [NR, 64]  lambda * LoRA-A of gate/up
   size_t pud;         // bf16 [NR, 64]  lambda * LoRA-A of down (hi/lo pairs)
+  size_t upart;       // fp32 [kLoraSplit, NR, 32] K-split partials of the gate/up LoRA-A
   size_t x16;         // fp16 [T, H]    x * 2^-ex (prefill)
   size_t ex;          // int32 [T]
   size_t hf;          // fp32 [NR, I]   h in sorted rows
@@ -59,6 +60,7 @@ inline WsLayout ws_layout(const moe_dims_t& d, int T, bool prefill) {
   W.gblob = o;      o = align256(o + (prefill ? (E + 1) * 8 : 0));
   W.pu = o;         o = align256(o + NR * kLoraK * 2);
   W.pud = o;        o = align256(o + NR * kLoraK * 2);
+  W.upart = o;      o = align256(o + size_t(kLoraSplit) * NR * 32 * 4);
   const size_t TP = prefill ? size_t(T) : 0;
   W.x16 = o;        o = align256(o + TP * d.H * 2);
   W.ex = o;         o = align256(o + TP * 4);
