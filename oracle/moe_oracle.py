@@ -30,6 +30,12 @@ Readings where the pages are silent:
     an unmerged LoRA delta lambda * B (A v).
   * shared expert output is scaled by sigmoid(shared-gate logit).
   * stacks: x_l = bf16(RMSNorm(h_l)), h_{l+1} = bf16(h_l + MoE_l(x_l)).
+  * prediction-as-routing ([P3] "三件套" Prerouter bullet: the prediction is
+    used as the route; [P2] Prerouter paragraph: predicted routes take part
+    in the real execution): the given experts replace the top-K selection,
+    in the given order; the router still runs, and their weights are the
+    same softmax of the router logits restricted to them (renormalised with
+    norm_topk).
 """
 from __future__ import annotations
 
@@ -209,7 +215,7 @@ def expert_forward(ex, x, lam: float, return_hidden=False):
 
 
 def moe_block(w, router, expert_of, x_bits, bias=None, shared=None,
-              return_parts=False):
+              return_parts=False, exec_idx=None):
     """Full MoE block for T tokens, one token at a time by definition.
 
     w: workload dict (H, E, K, lora_scale, n_shared, norm_topk optional);
@@ -222,6 +228,9 @@ def moe_block(w, router, expert_of, x_bits, bias=None, shared=None,
     Prefill evaluates the same per-token result: the pages' prefill/decode
     paragraph ([P2]) changes how experts are loaded and batched, not what each
     token computes.
+
+    exec_idx [T, K] (prediction-as-routing): execute these experts instead of
+    the router's top-K; weights as topk_weights over the given experts.
     """
     K = w["K"]
     lam = float(w["lora_scale"])
@@ -232,7 +241,7 @@ def moe_block(w, router, expert_of, x_bits, bias=None, shared=None,
     idx = np.zeros((T, K), dtype=np.int64)
     wts = np.zeros((T, K))
     for t in range(T):
-        idx[t] = select_topk(logits[t], K)
+        idx[t] = select_topk(logits[t], K) if exec_idx is None else np.asarray(exec_idx)[t]
         wts[t] = topk_weights(logits[t], idx[t], norm)
     n_slots = K + (1 if shared is not None else 0)
     y = np.zeros((T, n_slots, x.shape[1]))
@@ -281,7 +290,7 @@ def rmsnorm(h, eps: float) -> np.ndarray:
 
 
 def stack_layer(w, router, expert_of, h_bits, shared=None, eps=1e-6,
-                return_parts=False):
+                return_parts=False, exec_idx=None):
     """One decoder-free stack layer: h' = bf16(h + MoE(bf16(RMSNorm(h)))).
 
     Attention is replaced by the identity in the stacked workloads, so layers
@@ -291,7 +300,7 @@ def stack_layer(w, router, expert_of, h_bits, shared=None, eps=1e-6,
     h = bf16_to_f64(h_bits)
     xn_bits = round_bf16(rmsnorm(h, eps))
     res = moe_block(w, router, expert_of, xn_bits, shared=shared,
-                    return_parts=return_parts)
+                    return_parts=return_parts, exec_idx=exec_idx)
     o, parts = (res if return_parts else (res, None))
     out = round_bf16(h + o)
     if return_parts:

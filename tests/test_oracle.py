@@ -258,15 +258,16 @@ def _brute_proj(ex, p, v, lam):
     return res
 
 
-def _brute_block(w, router, experts, shared, xbits):
-    """Loop formulation of the block for one token, from the definitions."""
+def _brute_block(w, router, experts, shared, xbits, given=None):
+    """Loop formulation of the block for one token, from the definitions.
+    given: experts to execute in place of the top-K (prediction-as-routing)."""
     H, E, K, lam = w["H"], w["E"], w["K"], w["lora_scale"]
     x = [bfv(v) for v in xbits]
     logits = []
     for e in range(E):
         logits.append(math.fsum(float(router["router_s"][e][i // 64]) *
                                 int(router["router_q"][e][i]) * x[i] for i in range(H)))
-    order = sorted(range(E), key=lambda e: (-logits[e], e))[:K]
+    order = sorted(range(E), key=lambda e: (-logits[e], e))[:K] if given is None else list(given)
     m = max(logits)
     den = math.fsum(math.exp(v - m) for v in logits)
     p = [math.exp(logits[e] - m) / den for e in order]
@@ -473,3 +474,59 @@ def test_prerouter_feat_pins():
     pb, zb2 = O.prerouter_feat(W1b, W2b, h, np.array([[2, 3, 4], [3, 4, 6]], np.int32), K)
     assert pb[0, 0] == 5 and zb2[0, 5] > 39
     assert np.all(zb2[1] == 0) and pb[1].tolist() == [0, 1, 2]
+
+
+# --------------------------------------------------------------------------
+# prediction-as-routing: given experts replace the top-K
+# --------------------------------------------------------------------------
+def test_given_experts_brute_force_loops():
+    # the given experts are the two LOWEST-logit experts, in reverse order, so
+    # a path that ignored them, re-sorted them or took weights from the top-K
+    # would fail
+    w = synth.workload(0, H=128, E=6, K=2, I=64, r=3, n_shared=1)
+    router = synth.router_tensors(w, 0, seed=9)
+    experts = [synth.expert_tensors(w, 0, e, seed=9) for e in range(w["E"])]
+    shared = synth.expert_tensors(w, 0, w["E"], seed=9)
+    x = synth.tokens(w, 0, T=2, seed=9)
+    logits = O.router_logits(router["router_q"], router["router_s"], x)
+    given = np.stack([np.argsort(logits[t], kind="stable")[:2][::-1] for t in range(2)])
+    for t in range(2):
+        assert set(given[t]).isdisjoint(O.select_topk(logits[t], 2))
+    o, parts = O.moe_block(w, router, lambda e: experts[e], x, shared=shared,
+                           return_parts=True, exec_idx=given)
+    assert parts["idx"].tolist() == given.tolist()
+    for t in range(2):
+        order, want = _brute_block(w, router, experts, shared, x[t], given=given[t])
+        assert np.allclose(o[t], want, rtol=1e-11, atol=1e-11 * np.abs(want).max())
+
+
+def test_given_experts_weights_closed_form():
+    # logits 3, 1, 0 (exact): executing experts (2, 1) weighs them by the
+    # softmax of their own logits, 1/(1+e) and e/(1+e), renormalised; without
+    # renormalisation they keep their full-softmax shares
+    H = 64
+    rq, rs = _router_from_codes([3, 1, 0], 1.0 / H, H)
+    x = np.full((1, H), f2bits(1.0), np.uint16)
+    l = O.router_logits(rq, rs, x)[0]
+    assert list(l) == [3.0, 1.0, 0.0]
+    e = math.e
+    w = O.topk_weights(l, [2, 1])
+    assert np.allclose(w, [1 / (1 + e), e / (1 + e)], rtol=1e-15, atol=0)
+    z = e ** 3 + e + 1
+    w = O.topk_weights(l, [2, 1], norm_topk=False)
+    assert np.allclose(w, [1 / z, e / z], rtol=1e-15, atol=0)
+
+
+def test_given_experts_equal_to_topk_reduce_to_router_path():
+    w = synth.workload(0)
+    router = synth.router_tensors(w, 0, seed=3)
+    experts = [synth.expert_tensors(w, 0, e, seed=3) for e in range(w["E"])]
+    shared = synth.expert_tensors(w, 0, w["E"], seed=3)
+    x = synth.tokens(w, 0, T=3, seed=3)
+    o_r, parts = O.moe_block(w, router, lambda e: experts[e], x, shared=shared, return_parts=True)
+    o_g = O.moe_block(w, router, lambda e: experts[e], x, shared=shared, exec_idx=parts["idx"])
+    np.testing.assert_array_equal(o_g, o_r)
+    # a reordering of the given experts changes only the summation order
+    o_p = O.moe_block(w, router, lambda e: experts[e], x, shared=shared,
+                      exec_idx=parts["idx"][:, ::-1])
+    assert np.allclose(o_p, o_r, rtol=1e-13, atol=1e-13 * np.abs(o_r).max())
