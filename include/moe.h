@@ -117,13 +117,22 @@ MOE_API moe_status_t moe_pack_expert(int32_t H, int32_t I, int32_t r,
  *                   is read from here over PCIe.  Required when
  *                   expert_to_slot is not NULL.
  *   counters        device uint64 [2] or NULL: counters[0] += lookups served
- *                   from a slot, counters[1] += all lookups. */
+ *                   from a slot, counters[1] += all lookups.
+ *   read_delay_ns   modeled storage latency of the host copy ([P2] Prerouter
+ *                   and SSD paragraphs: the benefit of early loads grows with
+ *                   storage latency): in moe_block_decode(_exec), a
+ *                   workgroup that reads a non-resident expert first waits
+ *                   this long (a bounded wall-clock wait).  0: none; at most
+ *                   MOE_MAX_READ_DELAY_NS (else MOE_EINVAL).  The other
+ *                   calls ignore it. */
+#define MOE_MAX_READ_DELAY_NS 1000000u
 typedef struct {
   const void* slots;
   int32_t n_slots;
   const int32_t* expert_to_slot;
   const void* host_blobs;
   unsigned long long* counters;
+  uint32_t read_delay_ns;
 } moe_experts_t;
 
 /* Workspace bytes needed by moe_route + moe_expert_forward (+ prefill
@@ -235,6 +244,31 @@ MOE_API moe_status_t moe_block_decode(const moe_dims_t* d, const int8_t* gate_q,
                                       int32_t flags, float eps, int32_t* topk_idx, float* topk_w,
                                       uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_block_decode_exec: moe_block_decode with the routed experts given
+ * instead of selected (prediction-as-routing).  [P3] "三件套" Prerouter
+ * bullet: the predicted route is used as the route, so expert loads can
+ * overlap the forward pass; [P2] Prerouter paragraph: predicted routes take
+ * part in the actual execution.
+ *   exec_idx  device int32 [T, K]: the experts token t executes, in this
+ *             order (typically the previous token's Prerouter prediction for
+ *             this layer).  The router still runs: the weights are the
+ *             softmax of its logits over the given experts (renormalised
+ *             when d->norm_topk, else their full-softmax entries), and the
+ *             shared gate is unchanged.  topk_idx / topk_w (optional) get
+ *             the executed experts and their weights.
+ *   An entry outside [0, E) sets the sticky error word (as a wait that
+ *   exceeds its bound does) and is executed as expert 0.  Other arguments,
+ *   limits and the workspace are those of moe_block_decode (the same
+ *   workspace may serve both calls, in stream order). */
+MOE_API moe_status_t moe_block_decode_exec(const moe_dims_t* d, const int8_t* gate_q,
+                                           const float* gate_s, const int8_t* sgate_q,
+                                           const float* sgate_s, const moe_experts_t* routed,
+                                           const void* shared_blob, const uint16_t* h_in,
+                                           int32_t T, int32_t flags, float eps,
+                                           const int32_t* exec_idx, int32_t* topk_idx,
+                                           float* topk_w, uint16_t* out, void* ws,
+                                           size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * prerouter_predict: the Prerouter head.  [P1] Prerouter paragraph and [P2]
  * double-shift paragraph: a light MLP after layer N predicts layer N+1's
@@ -321,6 +355,13 @@ MOE_API moe_status_t moe_pool_create(int32_t n_layers, int32_t E, int32_t n_slot
                                      void* device_slots, int32_t* device_table,
                                      const void* host_blobs, void* stream, moe_pool_t** out);
 MOE_API void moe_pool_destroy(moe_pool_t* p);
+/* Modeled storage latency of the master copy (0: none, at most
+ * MOE_MAX_READ_DELAY_NS, else MOE_EINVAL).  Each moe_pool_update whose plan
+ * has fills starts them with one wait of this length on side_stream (the
+ * step's reads are issued together and complete after one latency), and
+ * moe_pool_layer reports it as read_delay_ns, so kernels that read a
+ * non-resident expert on demand pay it too. */
+MOE_API moe_status_t moe_pool_set_read_delay(moe_pool_t* p, uint32_t ns);
 /* The moe_experts_t of one layer (counters may be NULL). */
 MOE_API moe_status_t moe_pool_layer(const moe_pool_t* p, int32_t layer, unsigned long long* counters,
                                     moe_experts_t* out);
@@ -336,6 +377,11 @@ MOE_API moe_status_t moe_pool_update(moe_pool_t* p, const int32_t* executed, int
  * the layer had no fills since the last wait).  Call before a kernel that
  * reads the layer's table. */
 MOE_API moe_status_t moe_pool_wait_layer(moe_pool_t* p, int32_t layer, void* stream);
+/* Make `stream` wait until the last update's fills of `layer` are complete
+ * and its table row is final (no-op if the layer had no fills since the last
+ * wait): every expert the update filled for the layer is then read from its
+ * slot.  Used when the next step executes the predicted experts. */
+MOE_API moe_status_t moe_pool_wait_layer_filled(moe_pool_t* p, int32_t layer, void* stream);
 /* Host wait for all enqueued fills. */
 MOE_API moe_status_t moe_pool_sync(moe_pool_t* p, void* side_stream);
 /* The pool's planner (for moe_lru_table / moe_lru_stats). */

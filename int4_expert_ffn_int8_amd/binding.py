@@ -38,7 +38,7 @@ class MoePoolFill(ctypes.Structure):
 
 class MoeExperts(ctypes.Structure):
     _fields_ = [("slots", c_vp), ("n_slots", c_i32), ("expert_to_slot", c_vp),
-                ("host_blobs", c_vp), ("counters", c_vp)]
+                ("host_blobs", c_vp), ("counters", c_vp), ("read_delay_ns", ctypes.c_uint32)]
 
 
 _lib = None
@@ -61,6 +61,9 @@ _SIGS = {
     "moe_block_decode": (c_i32, [ctypes.POINTER(MoeDims), c_vp, c_vp, c_vp, c_vp,
                                  ctypes.POINTER(MoeExperts), c_vp, c_vp, c_i32, c_i32, c_f32,
                                  c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "moe_block_decode_exec": (c_i32, [ctypes.POINTER(MoeDims), c_vp, c_vp, c_vp, c_vp,
+                                      ctypes.POINTER(MoeExperts), c_vp, c_vp, c_i32, c_i32, c_f32,
+                                      c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "prerouter_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32]),
     "moe_lru_create": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_vp)]),
     "moe_lru_destroy": (None, [c_vp]),
@@ -76,6 +79,8 @@ _SIGS = {
     "moe_pool_update": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_vp,
                                 ctypes.POINTER(c_i32)]),
     "moe_pool_wait_layer": (c_i32, [c_vp, c_i32, c_vp]),
+    "moe_pool_wait_layer_filled": (c_i32, [c_vp, c_i32, c_vp]),
+    "moe_pool_set_read_delay": (c_i32, [c_vp, ctypes.c_uint32]),
     "moe_pool_sync": (c_i32, [c_vp, c_vp]),
     "moe_pool_lru": (c_vp, [c_vp]),
     "prerouter_predict": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_i32, c_vp,
@@ -89,10 +94,12 @@ HEADER_SYMBOLS = [
     "moe_last_error", "moe_expert_blob_bytes", "moe_pack_expert", "moe_workspace_bytes",
     "moe_route", "moe_expert_forward", "moe_combine", "moe_rmsnorm",
     "moe_block_decode_workspace_bytes", "moe_workspace_init", "moe_block_decode",
+    "moe_block_decode_exec",
     "prerouter_workspace_bytes", "prerouter_predict", "prerouter_predict_feat",
     "moe_lru_create", "moe_lru_destroy", "moe_lru_plan", "moe_lru_table", "moe_lru_stats",
     "moe_pool_create", "moe_pool_destroy", "moe_pool_layer", "moe_pool_update",
-    "moe_pool_wait_layer", "moe_pool_sync", "moe_pool_lru",
+    "moe_pool_wait_layer", "moe_pool_wait_layer_filled", "moe_pool_set_read_delay",
+    "moe_pool_sync", "moe_pool_lru",
 ]
 
 DECODE_NORM_INPUT = 1
@@ -180,8 +187,9 @@ def moe_route(d, gate_q, gate_s, sgate_q, sgate_s, x, T, logit_bias, topk_idx, t
 
 
 def experts_struct(slots, n_slots, expert_to_slot=None, host_blobs=None,
-                   counters=None) -> MoeExperts:
-    return MoeExperts(ptr(slots), n_slots, ptr(expert_to_slot), ptr(host_blobs), ptr(counters))
+                   counters=None, read_delay_ns: int = 0) -> MoeExperts:
+    return MoeExperts(ptr(slots), n_slots, ptr(expert_to_slot), ptr(host_blobs), ptr(counters),
+                      read_delay_ns)
 
 
 def moe_expert_forward(d, routed: MoeExperts, shared_blob, x, T, topk_idx, counts, offsets,
@@ -239,6 +247,17 @@ def moe_block_decode(d, gate_q, gate_s, sgate_q, sgate_s, routed: MoeExperts, sh
                                    ptr(out), ptr(ws),
                                    ws.numel() * ws.element_size() if ws is not None else 0,
                                    stream_ptr(stream)))
+
+
+def moe_block_decode_exec(d, gate_q, gate_s, sgate_q, sgate_s, routed: MoeExperts, shared_blob,
+                          h_in, T, flags, eps, exec_idx, topk_idx, topk_w, out, ws,
+                          stream=None) -> None:
+    _check(load().moe_block_decode_exec(ctypes.byref(d), ptr(gate_q), ptr(gate_s), ptr(sgate_q),
+                                        ptr(sgate_s), ctypes.byref(routed), ptr(shared_blob),
+                                        ptr(h_in), T, flags, eps, ptr(exec_idx), ptr(topk_idx),
+                                        ptr(topk_w), ptr(out), ptr(ws),
+                                        ws.numel() * ws.element_size() if ws is not None else 0,
+                                        stream_ptr(stream)))
 
 
 # ---- expert pool ------------------------------------------------------------
@@ -326,6 +345,12 @@ class MoePool:
 
     def wait_layer(self, layer: int, stream=None) -> None:
         _check(load().moe_pool_wait_layer(self.h, layer, stream_ptr(stream)))
+
+    def wait_layer_filled(self, layer: int, stream=None) -> None:
+        _check(load().moe_pool_wait_layer_filled(self.h, layer, stream_ptr(stream)))
+
+    def set_read_delay(self, ns: int) -> None:
+        _check(load().moe_pool_set_read_delay(self.h, int(ns)))
 
     def sync(self, side_stream=None) -> None:
         _check(load().moe_pool_sync(self.h, stream_ptr(side_stream)))

@@ -246,14 +246,30 @@ extern "C" moe_status_t moe_workspace_init(void* ws, size_t ws_bytes, void* stre
                     fn);
 }
 
-extern "C" moe_status_t moe_block_decode(const moe_dims_t* d, const int8_t* gate_q,
-                                         const float* gate_s, const int8_t* sgate_q,
-                                         const float* sgate_s, const moe_experts_t* routed,
-                                         const void* shared_blob, const uint16_t* h_in, int32_t T,
-                                         int32_t flags, float eps, int32_t* topk_idx,
-                                         float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
-                                         void* stream) {
-  const char* fn = "moe_block_decode";
+namespace moe {
+
+uint32_t wall_ticks(uint32_t ns) {
+  if (ns == 0) return 0;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) {
+    (void)hipGetLastError();
+    khz = 100000;  // the 100 MHz constant-rate clock of CDNA parts
+  }
+  const uint64_t t = (uint64_t(ns) * uint64_t(khz) + 999999u) / 1000000u;
+  return uint32_t(t > 0xFFFFFFFFull ? 0xFFFFFFFFull : t);
+}
+
+}  // namespace moe
+
+namespace {
+
+moe_status_t block_decode(const char* fn, const moe_dims_t* d, const int8_t* gate_q,
+                          const float* gate_s, const int8_t* sgate_q, const float* sgate_s,
+                          const moe_experts_t* routed, const void* shared_blob,
+                          const uint16_t* h_in, int32_t T, int32_t flags, float eps,
+                          const int32_t* exec_idx, int32_t* topk_idx, float* topk_w,
+                          uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
   moe_status_t st = check_dims(d, fn);
   if (st != MOE_OK) return st;
   if (T < 0) return fail(MOE_EINVAL, "%s: T=%d is negative", fn, T);
@@ -276,6 +292,9 @@ extern "C" moe_status_t moe_block_decode(const moe_dims_t* d, const int8_t* gate
     return fail(MOE_EINVAL, "%s: n_shared=1 needs shared_blob, sgate_q and sgate_s", fn);
   if ((flags & MOE_DECODE_NORM_INPUT) && !(eps >= 0.f && isfinite(eps)))
     return fail(MOE_EINVAL, "%s: eps must be finite and >= 0", fn);
+  if (routed->read_delay_ns > MOE_MAX_READ_DELAY_NS)
+    return fail(MOE_EINVAL, "%s: read_delay_ns=%u exceeds %u", fn, routed->read_delay_ns,
+                MOE_MAX_READ_DELAY_NS);
   if (T == 0) return MOE_OK;
   if (!gate_q || !gate_s || !h_in || !out) return fail(MOE_EINVAL, "%s: null pointer", fn);
   const FusedWs W = fused_ws_layout(T, d->E, d->K, d->n_shared, d->I, d->r);
@@ -305,11 +324,13 @@ extern "C" moe_status_t moe_block_decode(const moe_dims_t* d, const int8_t* gate
   a.src.host_blobs = static_cast<const uint8_t*>(routed->host_blobs);
   a.src.counters = routed->counters;
   a.src.stride = a.L.total;
+  a.src.delay_ticks = routed->expert_to_slot ? wall_ticks(routed->read_delay_ns) : 0;
   a.shared_blob = static_cast<const uint8_t*>(shared_blob);
   a.h_in = h_in;
   a.out = out;
   a.user_idx = topk_idx;
   a.user_w = topk_w;
+  a.exec_idx = exec_idx;
   a.sync = reinterpret_cast<int*>(wsb + W.sync);
   a.logits = reinterpret_cast<tword_t*>(wsb + W.logits);
   a.route = reinterpret_cast<tword_t*>(wsb + W.route);
@@ -319,4 +340,33 @@ extern "C" moe_status_t moe_block_decode(const moe_dims_t* d, const int8_t* gate
   a.hexp = reinterpret_cast<tword_t*>(wsb + W.hexp);
   a.vpart = reinterpret_cast<tword_t*>(wsb + W.vpart);
   return hip_status(launch_fused(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+extern "C" moe_status_t moe_block_decode(const moe_dims_t* d, const int8_t* gate_q,
+                                         const float* gate_s, const int8_t* sgate_q,
+                                         const float* sgate_s, const moe_experts_t* routed,
+                                         const void* shared_blob, const uint16_t* h_in, int32_t T,
+                                         int32_t flags, float eps, int32_t* topk_idx,
+                                         float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  return block_decode("moe_block_decode", d, gate_q, gate_s, sgate_q, sgate_s, routed,
+                      shared_blob, h_in, T, flags, eps, nullptr, topk_idx, topk_w, out, ws,
+                      ws_bytes, stream);
+}
+
+extern "C" moe_status_t moe_block_decode_exec(const moe_dims_t* d, const int8_t* gate_q,
+                                              const float* gate_s, const int8_t* sgate_q,
+                                              const float* sgate_s, const moe_experts_t* routed,
+                                              const void* shared_blob, const uint16_t* h_in,
+                                              int32_t T, int32_t flags, float eps,
+                                              const int32_t* exec_idx, int32_t* topk_idx,
+                                              float* topk_w, uint16_t* out, void* ws,
+                                              size_t ws_bytes, void* stream) {
+  if (T > 0 && exec_idx == nullptr)
+    return fail(MOE_EINVAL, "moe_block_decode_exec: exec_idx is NULL");
+  return block_decode("moe_block_decode_exec", d, gate_q, gate_s, sgate_q, sgate_s, routed,
+                      shared_blob, h_in, T, flags, eps, exec_idx, topk_idx, topk_w, out, ws,
+                      ws_bytes, stream);
 }

@@ -171,4 +171,11 @@ __device__ __forceinline__ uint4 gload16(const void* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Wait `ticks` periods of the constant-rate wall clock.  The bound is the
+// argument itself, so the loop always ends.
+__device__ __forceinline__ void wall_wait(uint32_t ticks) {
+  const uint64_t t0 = uint64_t(wall_clock64());
+  while (uint64_t(wall_clock64()) - t0 < ticks) __builtin_amdgcn_s_sleep(8);
+}
+
 }  // namespace moe

@@ -45,6 +45,7 @@ struct FusedArgs {
   uint16_t* out;         // [T][H] bf16
   int32_t* user_idx;     // [T][K] or null
   float* user_w;         // [T][K] or null
+  const int32_t* exec_idx;  // [T][K] experts to execute (prediction-as-routing) or null
   // workspace
   int* sync;
   tword_t* logits;  // [T][E + 1]   router logits; column E: shared-gate logit

@@ -119,7 +119,9 @@ __device__ __forceinline__ const uint8_t* expert_blob(const FusedArgs& a, int e,
     atomicAdd(&a.src.counters[1], 1ull);
     if (s >= 0) atomicAdd(&a.src.counters[0], 1ull);
   }
-  return s >= 0 ? a.src.slots + size_t(s) * a.src.stride : a.src.host_blobs + size_t(e) * a.src.stride;
+  if (s >= 0) return a.src.slots + size_t(s) * a.src.stride;
+  if (a.src.delay_ticks) wall_wait(a.src.delay_ticks);  // modeled storage latency
+  return a.src.host_blobs + size_t(e) * a.src.stride;
 }
 
 // Expert id of routed pair p, published by the top-K (workgroup-uniform).
@@ -245,15 +247,48 @@ __device__ void role_router(const FusedArgs& a, int b) {
     }
     float first = 0.f, denom = 0.f, mine = 0.f;
     int mine_e = 0;
-    topk_wave(v, a.E, a.K, lane, [&](int k, float mx, uint32_t sel) {
-      if (k == 0) first = mx;
-      const float ev = expf(mx - first);
-      denom += ev;
-      if (k == lane) {
-        mine = ev;
-        mine_e = int(sel);
+    if (a.exec_idx == nullptr) {
+      topk_wave(v, a.E, a.K, lane, [&](int k, float mx, uint32_t sel) {
+        if (k == 0) first = mx;
+        const float ev = expf(mx - first);
+        denom += ev;
+        if (k == lane) {
+          mine = ev;
+          mine_e = int(sel);
+        }
+      });
+    } else {
+      // given experts: lane k < K takes expert exec_idx[t][k] and fetches its
+      // logit from the lane that holds it
+      if (lane < a.K) {
+        mine_e = a.exec_idx[t * a.K + lane];
+        if (uint32_t(mine_e) >= uint32_t(a.E)) {
+          set_err(a);
+          mine_e = 0;
+        }
       }
-    });
+      float gl = 0.f;
+#pragma unroll
+      for (int m = 0; m < MP; ++m) {
+        if (64 * m >= a.E) break;
+        const float c = __shfl(v[m], mine_e & 63);
+        if ((mine_e >> 6) == m) gl = c;
+      }
+      first = wave_max(lane < a.K ? gl : -INFINITY);
+      mine = lane < a.K ? expf(gl - first) : 0.f;
+      // summed in k order, as the selection path does: given experts equal
+      // to the router's top-K reproduce its weights bit for bit
+      for (int k = 0; k < a.K; ++k) denom += __shfl(mine, k);
+      if (!a.norm_topk) {  // the full-softmax form below subtracts the largest logit
+        float mx = -INFINITY;
+#pragma unroll
+        for (int m = 0; m < MP; ++m)
+          if (lane + 64 * m < a.E) mx = fmaxf(mx, v[m]);
+        const float top = wave_max(mx);
+        mine = lane < a.K ? expf(gl - top) : 0.f;
+        first = top;
+      }
+    }
     if (!a.norm_topk) {  // full-softmax entries: denominator over all E
       float part = 0.f;
 #pragma unroll
@@ -673,6 +708,13 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t st) {
 
 __global__ void k_zero_ints(int* p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+__global__ void k_storage_delay(uint32_t ticks) { wall_wait(ticks); }
+
+hipError_t launch_storage_delay(uint32_t ticks, hipStream_t st) {
+  hipLaunchKernelGGL(k_storage_delay, dim3(1), dim3(1), 0, st, ticks);
+  return hipGetLastError();
 }
 
 hipError_t launch_zero_ints(int* p, int n, hipStream_t st) {

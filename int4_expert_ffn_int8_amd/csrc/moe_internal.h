@@ -69,6 +69,12 @@ struct ExpertSource {
   const uint8_t* host_blobs;
   unsigned long long* counters;
   size_t stride;
+  uint32_t delay_ticks = 0;  // modeled storage latency of a host read, wall-clock ticks
 };
+
+// Host: ns -> ticks of the device's constant-rate wall clock (current device).
+uint32_t wall_ticks(uint32_t ns);
+// One wait of `ticks` wall-clock ticks on stream st (a single-lane kernel).
+hipError_t launch_storage_delay(uint32_t ticks, hipStream_t st);
 
 }  // namespace moe

@@ -10,10 +10,13 @@
 //
 // Ordering.  A fill of slot s (evicting expert a, loading expert b) runs on a
 // side stream as: (1) table row with a -> -1, (2) event inv[layer], (3) copy
-// of b's blob into s, (4) table row with b -> s.  A kernel of that layer that
-// starts after inv[layer] never maps a to s, and sees b -> s only once the
-// copy is complete; kernels that used a were finished before the plan was
-// made (the caller plans after the previous token completed).
+// of b's blob into s, (4) table row with b -> s, (5) event filled[layer].  A
+// kernel of that layer that starts after inv[layer] never maps a to s, and
+// sees b -> s only once the copy is complete; kernels that used a were
+// finished before the plan was made (the caller plans after the previous
+// token completed).  A kernel that starts after filled[layer] finds every
+// expert of the plan in its slot (prediction-as-routing waits for that).
+// With a modeled storage latency, one wait kernel precedes the plan's copies.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -21,6 +24,7 @@
 #include <new>
 #include <vector>
 
+#include "moe_internal.h"
 #include "status.h"
 
 namespace {
@@ -50,6 +54,9 @@ struct moe_pool {
   int32_t* staging = nullptr;       // pinned [2][n_layers][E]
   std::vector<hipEvent_t> inv;      // per layer
   std::vector<char> inv_pending;    // per layer: inv[layer] recorded since last wait
+  std::vector<hipEvent_t> filled;   // per layer: after the fills and the final table row
+  std::vector<char> filled_pending;
+  uint32_t read_delay_ns = 0;       // modeled storage latency of the master copy
   std::vector<moe_pool_fill_t> plan;
 };
 
@@ -242,8 +249,12 @@ MOE_API moe_status_t moe_pool_create(int32_t n_layers, int32_t E, int32_t n_slot
   for (size_t i = 0; i < rows; ++i) p->staging[i] = -1;
   p->inv.assign(n_layers, nullptr);
   p->inv_pending.assign(n_layers, 0);
-  for (int32_t ly = 0; ly < n_layers && e == hipSuccess; ++ly)
+  p->filled.assign(n_layers, nullptr);
+  p->filled_pending.assign(n_layers, 0);
+  for (int32_t ly = 0; ly < n_layers && e == hipSuccess; ++ly) {
     e = hipEventCreateWithFlags(&p->inv[ly], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->filled[ly], hipEventDisableTiming);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (e == hipSuccess)
     e = hipMemcpyAsync(p->table, p->staging, size_t(n_layers) * E * sizeof(int32_t),
@@ -261,6 +272,8 @@ MOE_API void moe_pool_destroy(moe_pool_t* p) {
   if (p == nullptr) return;
   for (hipEvent_t ev : p->inv)
     if (ev) (void)hipEventDestroy(ev);
+  for (hipEvent_t ev : p->filled)
+    if (ev) (void)hipEventDestroy(ev);
   if (p->staging) (void)hipHostFree(p->staging);
   delete p;
 }
@@ -274,6 +287,15 @@ MOE_API moe_status_t moe_pool_layer(const moe_pool_t* p, int32_t layer, unsigned
   out->expert_to_slot = p->table + size_t(layer) * p->lru.E;
   out->host_blobs = p->host_dev + size_t(layer) * p->lru.E * p->blob_bytes;
   out->counters = counters;
+  out->read_delay_ns = p->read_delay_ns;
+  return MOE_OK;
+}
+
+MOE_API moe_status_t moe_pool_set_read_delay(moe_pool_t* p, uint32_t ns) {
+  if (p == nullptr) return fail(MOE_EINVAL, "moe_pool_set_read_delay: NULL pool");
+  if (ns > MOE_MAX_READ_DELAY_NS)
+    return fail(MOE_EINVAL, "moe_pool_set_read_delay: %u ns exceeds %u", ns, MOE_MAX_READ_DELAY_NS);
+  p->read_delay_ns = ns;
   return MOE_OK;
 }
 
@@ -290,6 +312,11 @@ MOE_API moe_status_t moe_pool_update(moe_pool_t* p, const int32_t* executed, int
   if (n_fills) *n_fills = int32_t(p->plan.size());
   const int32_t E = p->lru.E;
   const size_t row_bytes = size_t(E) * sizeof(int32_t);
+  if (!p->plan.empty() && p->read_delay_ns) {
+    // the step's reads are issued together: one storage latency before the copies
+    e = moe::launch_storage_delay(moe::wall_ticks(p->read_delay_ns), s);
+    if (e != hipSuccess) return fail(MOE_EHIP, "moe_pool_update: %s", hipGetErrorString(e));
+  }
   size_t i = 0;
   while (i < p->plan.size()) {
     const int32_t ly = p->plan[i].layer;
@@ -311,8 +338,10 @@ MOE_API moe_status_t moe_pool_update(moe_pool_t* p, const int32_t* executed, int
       e = hipMemcpyAsync(dst, src, p->blob_bytes, hipMemcpyHostToDevice, s);
     }
     if (e == hipSuccess) e = hipMemcpyAsync(dev_row, pub_row, row_bytes, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipEventRecord(p->filled[ly], s);
     if (e != hipSuccess) return fail(MOE_EHIP, "moe_pool_update: %s", hipGetErrorString(e));
     p->inv_pending[ly] = 1;
+    p->filled_pending[ly] = 1;
     i = j;
   }
   return MOE_OK;
@@ -325,6 +354,18 @@ MOE_API moe_status_t moe_pool_wait_layer(moe_pool_t* p, int32_t layer, void* str
   const hipError_t e = hipStreamWaitEvent(static_cast<hipStream_t>(stream), p->inv[layer], 0);
   if (e != hipSuccess) return fail(MOE_EHIP, "moe_pool_wait_layer: %s", hipGetErrorString(e));
   p->inv_pending[layer] = 0;
+  return MOE_OK;
+}
+
+MOE_API moe_status_t moe_pool_wait_layer_filled(moe_pool_t* p, int32_t layer, void* stream) {
+  if (p == nullptr || layer < 0 || layer >= p->lru.n_layers)
+    return fail(MOE_EINVAL, "moe_pool_wait_layer_filled: bad arguments");
+  if (!p->filled_pending[layer]) return MOE_OK;
+  const hipError_t e = hipStreamWaitEvent(static_cast<hipStream_t>(stream), p->filled[layer], 0);
+  if (e != hipSuccess)
+    return fail(MOE_EHIP, "moe_pool_wait_layer_filled: %s", hipGetErrorString(e));
+  p->filled_pending[layer] = 0;
+  p->inv_pending[layer] = 0;  // the fills follow the invalidation on the same stream
   return MOE_OK;
 }
 

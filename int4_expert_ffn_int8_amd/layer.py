@@ -132,12 +132,17 @@ class MoeLayer:
             "out": torch.empty((T, self.H), dtype=torch.int16, device=dv),
         }
 
-    def decode_fused(self, h_in, fb, flags=0, eps=1e-6, out=None, routed=None, stream=None):
-        """One kernel launch: route + experts + combine (+ norm / residual)."""
+    def decode_fused(self, h_in, fb, flags=0, eps=1e-6, out=None, routed=None, stream=None,
+                     exec_idx=None):
+        """One kernel launch: route + experts + combine (+ norm / residual).
+        exec_idx: device int32 [T, K] experts to execute instead of the top-K."""
         out = fb["out"] if out is None else out
-        B.moe_block_decode(self.d, self.gate_q, self.gate_s, self.sgate_q, self.sgate_s,
-                           routed or self.experts, self.shared_blob, h_in, fb["T"], flags, eps,
-                           fb["idx"], fb["w"], out, fb["ws"], stream)
+        args = (self.d, self.gate_q, self.gate_s, self.sgate_q, self.sgate_s,
+                routed or self.experts, self.shared_blob, h_in, fb["T"], flags, eps)
+        if exec_idx is None:
+            B.moe_block_decode(*args, fb["idx"], fb["w"], out, fb["ws"], stream)
+        else:
+            B.moe_block_decode_exec(*args, exec_idx, fb["idx"], fb["w"], out, fb["ws"], stream)
         return out
 
     @staticmethod
@@ -158,6 +163,13 @@ class MoeStack:
     host master copy; `end_step` commits the step (executed + predicted
     experts) to the pool, whose fills then overlap the next step.
 
+    exec_mode "router": every layer executes its router's top-K (the
+    predictions only steer the pool).  "predict" (prediction-as-routing,
+    [P3] "三件套" Prerouter bullet): layers 1 .. L-1 execute the experts that
+    the previous step's heads predicted for them, weighted by their router's
+    logits; with a pool, such a layer waits for its fills, so those experts
+    are read from HBM.  Layer 0, and every layer of the first step, route.
+
     routers: per layer dict(router_q, router_s, sgate_q, sgate_s);
     shared_blobs: device uint8 [L, blob] or None; routed: device uint8
     [L, E, blob] (all resident) or None with `host_blobs` (pinned uint8
@@ -167,7 +179,7 @@ class MoeStack:
 
     def __init__(self, H, I, E, K, r, n_shared, lora_scale, routers, shared_blobs, routed=None,
                  host_blobs=None, pool_slots=0, prerouter=None, pred_k=0, eps=1e-6,
-                 max_fills=-1, device="cuda"):
+                 max_fills=-1, exec_mode="router", device="cuda"):
         self.H, self.I, self.E, self.K, self.r, self.S = H, I, E, K, r, n_shared
         self.L = len(routers)
         self.d = B.dims(H, I, E, K, r, n_shared, lora_scale, 1)
@@ -194,6 +206,8 @@ class MoeStack:
             self.experts = [self.pool.layer(l, self.counters[l]) for l in range(self.L)]
         self.prerouter = prerouter
         self.pred_k = pred_k
+        self.exec_mode = "router"
+        self.have_pred = False
         T = 1
         self.ws = torch.empty((B.moe_block_decode_workspace_bytes(self.d, T),), dtype=torch.uint8,
                               device=dv)
@@ -206,33 +220,63 @@ class MoeStack:
             self.pr_ws = torch.empty((B.prerouter_workspace_bytes(D, E, T),), dtype=torch.uint8,
                                      device=dv)
             self.pred = torch.full((self.L, T, pred_k), -1, dtype=torch.int32, device=dv)
+            self.pred_exec = torch.full((self.L, T, pred_k), -1, dtype=torch.int32, device=dv)
         # step-boundary copies for the pool planner
         self.idx_host = torch.empty((self.L, K), dtype=torch.int32, pin_memory=True)
         self.pred_host = torch.full((self.L, max(pred_k, 1)), -1, dtype=torch.int32,
                                     pin_memory=True)
         self.done = torch.cuda.Event()
+        self.set_exec_mode(exec_mode)
+
+    def set_exec_mode(self, mode: str):
+        """Switch between router-executed and prediction-as-routing steps."""
+        if mode not in ("router", "predict"):
+            raise ValueError(f"exec_mode must be 'router' or 'predict', not {mode!r}")
+        if mode == "predict" and (self.prerouter is None or self.pred_k != self.K):
+            raise ValueError("prediction-as-routing needs Prerouter heads with pred_k == K")
+        self.exec_mode = mode
+        self.have_pred = False
+
+    def set_read_delay(self, ns: int):
+        """Modeled storage latency of the pool's master copy (see moe.h)."""
+        self.pool.set_read_delay(ns)
+        self.experts = [self.pool.layer(l, self.counters[l]) for l in range(self.L)]
 
     def layer_forward(self, l, h_in, out, stream=None):
         R = self.routers[l]
+        given = self.exec_mode == "predict" and self.have_pred and l > 0
         if self.pool is not None:
-            self.pool.wait_layer(l, stream)
-        B.moe_block_decode(self.d, R["router_q"], R["router_s"], R.get("sgate_q"),
-                           R.get("sgate_s"), self.experts[l],
-                           self.shared[l] if self.S else None, h_in, 1,
-                           B.DECODE_NORM_INPUT | B.DECODE_RESIDUAL, self.eps, self.idx[l],
-                           self.w[l], out, self.ws, stream)
+            if given:
+                self.pool.wait_layer_filled(l, stream)
+            else:
+                self.pool.wait_layer(l, stream)
+        args = (self.d, R["router_q"], R["router_s"], R.get("sgate_q"), R.get("sgate_s"),
+                self.experts[l], self.shared[l] if self.S else None, h_in, 1,
+                B.DECODE_NORM_INPUT | B.DECODE_RESIDUAL, self.eps)
+        if given:
+            B.moe_block_decode_exec(*args, self.pred_exec[l], self.idx[l], self.w[l], out,
+                                    self.ws, stream)
+        else:
+            B.moe_block_decode(*args, self.idx[l], self.w[l], out, self.ws, stream)
 
-    def step(self, x, stream=None):
-        """One token through every layer; returns the output hidden state."""
+    def step(self, x, stream=None, outs=None):
+        """One token through every layer; returns the output hidden state.
+        outs: optional per-layer output buffers (default: two alternating)."""
         cur = x
         for l in range(self.L):
-            out = self.h[l % 2]
+            out = self.h[l % 2] if outs is None else outs[l]
             self.layer_forward(l, cur, out, stream)
             if self.prerouter is not None and l + 1 < self.L:
                 W1, W2 = self.prerouter[l]
                 B.prerouter_predict(W1, W2, self.H, W1.shape[0], self.E, self.pred_k, out, 1,
                                     self.pred[l + 1], None, self.pr_ws, stream)
             cur = out
+        if self.exec_mode == "predict":
+            # this step's predictions are the next step's routes
+            s = torch.cuda.current_stream() if stream is None else stream
+            with torch.cuda.stream(s):
+                self.pred_exec.copy_(self.pred)
+            self.have_pred = True
         return cur
 
     def end_step(self, stream=None):
