@@ -74,6 +74,7 @@ extern "C" moe_status_t moe_route(const moe_dims_t* d, const int8_t* gate_q, con
   float* lg = logits ? logits : reinterpret_cast<float*>(wsb + W.logits);
   float* sg = reinterpret_cast<float*>(wsb + W.sg);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  float* plog = nullptr;  // K-split partial logits, summed by the top-K kernel
   if (T >= kRouterGemmMinT) {
     // many tokens: MFMA GEMM over int8 codes (exact in bf16), fp32 group
     // scale applied per 64-column chunk
@@ -92,7 +93,7 @@ extern "C" moe_status_t moe_route(const moe_dims_t* d, const int8_t* gate_q, con
     g.bias = logit_bias;
     g.logits = lg;
     g.sg_logit = sg;
-    g.plog = reinterpret_cast<float*>(wsb + W.plog);
+    g.plog = plog = reinterpret_cast<float*>(wsb + W.plog);
     st = hip_status(launch_router_gemm(g, s), fn);
   } else {
     st = hip_status(launch_router_logits(d->H, gate_q, gate_s, sgate_q, sgate_s, x, logit_bias,
@@ -100,9 +101,9 @@ extern "C" moe_status_t moe_route(const moe_dims_t* d, const int8_t* gate_q, con
                     fn);
   }
   if (st != MOE_OK) return st;
-  st = hip_status(
-      launch_topk(lg, sg, T, d->E, d->K, d->n_shared, d->norm_topk, topk_idx, topk_w, shared_w, s),
-      fn);
+  st = hip_status(launch_topk(lg, sg, T, d->E, d->K, d->n_shared, d->norm_topk, topk_idx, topk_w,
+                              shared_w, s, plog, plog ? kRouterSplit : 0, logit_bias),
+                  fn);
   if (st != MOE_OK || !group) return st;
   return hip_status(launch_group(topk_idx, T, d->K, d->E, counts, offsets, perm,
                                  reinterpret_cast<int32_t*>(wsb + W.chunk_hist),

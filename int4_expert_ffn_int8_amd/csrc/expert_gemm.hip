@@ -42,14 +42,88 @@ __device__ __forceinline__ int row_exp(float m) {
 }
 
 // ---------------------------------------------------------------------------
-// x [T][H] bf16 -> x16 [T][H] fp16 scaled by 2^-ex[t].  One wave per token.
-// grid ceil(T / 4), block 256.
-__global__ void __launch_bounds__(256) k_x16(const uint16_t* __restrict__ x, int T, int H,
-                                             uint16_t* __restrict__ x16, int32_t* __restrict__ ex) {
+// Expert-GEMM setup for the 256 threads of one workgroup: group row starts,
+// m-tile starts for tiles of kPrefillBM rows (exclusive scan over the experts
+// in order, 4 experts per thread), and each group's blob address (pool lookup
+// for routed experts with at least one token; one hit/lookup count each).
+__device__ __forceinline__ void expert_setup_block(const X16SetupArgs& a) {
+  __shared__ int wsum[4];
+  constexpr int EPT = kMaxE / 256;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tiles[EPT], cnt[EPT], local = 0;
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = tid * EPT + k;
+    cnt[k] = (e < a.E) ? a.counts[e] : 0;
+    tiles[k] = (cnt[k] + kPrefillBM - 1) / kPrefillBM;
+    local += tiles[k];
+  }
+  int inc = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int run = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) run += wsum[w];
+    total += wsum[w];
+  }
+  run += inc - local;
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) {
+    const int e = tid * EPT + k;
+    if (e < a.E) {
+      a.gstart[e] = a.offsets[e];
+      a.tstart[e] = run;
+      const ExpertSource& src = a.src;
+      const uint8_t* b;
+      if (src.expert_to_slot == nullptr) {
+        b = src.slots + size_t(e) * src.stride;
+      } else {
+        const int slot = src.expert_to_slot[e];
+        if (cnt[k] > 0 && src.counters) {
+          atomicAdd(&src.counters[1], 1ull);
+          if (slot >= 0) atomicAdd(&src.counters[0], 1ull);
+        }
+        b = slot >= 0 ? src.slots + size_t(slot) * src.stride : src.host_blobs + size_t(e) * src.stride;
+      }
+      a.gblob[e] = reinterpret_cast<unsigned long long>(b);
+    }
+    run += tiles[k];
+  }
+  if (tid == 0) {
+    const int TK = a.T * a.K;
+    a.gstart[a.E] = TK;
+    a.gstart[a.E + 1] = TK + a.S * a.T;
+    a.tstart[a.E] = total;
+    a.tstart[a.E + 1] = total + a.S * ((a.T + kPrefillBM - 1) / kPrefillBM);
+    a.gblob[a.E] = reinterpret_cast<unsigned long long>(a.shared_blob);
+  }
+}
+
+// Blocks 0 .. ceil(T/4) - 1: x [T][H] bf16 -> x16 [T][H] fp16 scaled by
+// 2^-ex[t], one wave per token, and zeros of the gate/up row maxima of their
+// tokens' rows; the last block: the expert-GEMM setup.  block 256.
+__global__ void __launch_bounds__(256) k_x16_setup(X16SetupArgs a) {
+  const int nx = (a.T + 3) / 4;
+  if (int(blockIdx.x) == nx) {
+    expert_setup_block(a);
+    return;
+  }
+  const int KS = a.K + a.S, NR = a.T * KS;
+  for (int i = threadIdx.x; i < 4 * KS; i += 256) {
+    const int r = blockIdx.x * 4 * KS + i;
+    if (r < NR) a.hmax[r] = 0u;
+  }
+  const int H = a.H;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const uint4* src = reinterpret_cast<const uint4*>(x + size_t(t) * H);
+  if (t >= a.T) return;
+  const uint4* src = reinterpret_cast<const uint4*>(a.x + size_t(t) * H);
   float m = 0.f;
   for (int i = lane; i < H / 8; i += 64) {
     const uint4 v = src[i];
@@ -59,7 +133,7 @@ __global__ void __launch_bounds__(256) k_x16(const uint16_t* __restrict__ x, int
   }
   m = wave_max(m);
   const int e = row_exp(m);
-  uint4* dst = reinterpret_cast<uint4*>(x16 + size_t(t) * H);
+  uint4* dst = reinterpret_cast<uint4*>(a.x16 + size_t(t) * H);
   for (int i = lane; i < H / 8; i += 64) {
     const uint4 v = src[i];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -71,7 +145,7 @@ __global__ void __launch_bounds__(256) k_x16(const uint16_t* __restrict__ x, int
     }
     dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
   }
-  if (lane == 0) ex[t] = e;
+  if (lane == 0) a.ex[t] = e;
 }
 
 // h [NR][I] fp32 -> hs16 [NR][I] fp16 scaled by 2^-eh[s], with the row maxima
@@ -465,8 +539,9 @@ int expert_gemm_blocks(int mtiles, int nrows) {
   return 8 * ((mtiles + 7) / 8) * ((nrows + EBN - 1) / EBN);
 }
 
-hipError_t launch_x16(const uint16_t* x, int T, int H, uint16_t* x16, int32_t* ex, hipStream_t st) {
-  if (T > 0) hipLaunchKernelGGL(k_x16, dim3((T + 3) / 4), dim3(256), 0, st, x, T, H, x16, ex);
+hipError_t launch_x16_setup(const X16SetupArgs& a, hipStream_t st) {
+  if (a.E > kMaxE) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_x16_setup, dim3((a.T + 3) / 4 + 1), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -63,7 +63,23 @@ hipError_t launch_prefill_experts(const GemmArgs& a, const int32_t* counts, Expe
                                   const uint8_t* shared_blob, uint16_t* x16, int32_t* ex,
                                   uint16_t* hs16, int32_t* eh, hipStream_t st);
 // expert_gemm.hip
-hipError_t launch_x16(const uint16_t* x, int T, int H, uint16_t* x16, int32_t* ex, hipStream_t st);
+// x to fp16 with a row exponent, zeros of the gate/up row maxima, and the
+// expert-GEMM setup (group row starts, tile starts, blob addresses), in one launch
+struct X16SetupArgs {
+  const uint16_t* x;  // [T][H] bf16
+  int T, H, E, K, S;
+  uint16_t* x16;      // [T][H]
+  int32_t* ex;        // [T]
+  uint32_t* hmax;     // [T * (K + S)]
+  const int32_t* counts;   // [E]
+  const int32_t* offsets;  // [E + 1]
+  ExpertSource src;
+  const uint8_t* shared_blob;
+  int32_t* gstart;           // [E + 2]
+  int32_t* tstart;           // [E + 2]
+  unsigned long long* gblob; // [E + 1]
+};
+hipError_t launch_x16_setup(const X16SetupArgs& a, hipStream_t st);
 hipError_t launch_h16(const float* h, const uint32_t* hmax, const int32_t* nrows, int NR, int I,
                       uint16_t* hs16, int32_t* eh, hipStream_t st);
 hipError_t launch_expert_gemm(int mode, const GemmArgs& a, int mtiles, hipStream_t st);

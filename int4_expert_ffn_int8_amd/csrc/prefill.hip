@@ -127,51 +127,6 @@ __global__ void __launch_bounds__(1024) k_group_scatter(const int32_t* __restric
   }
 }
 
-// Expert-GEMM setup (one workgroup): group row starts, m-tile starts for
-// tiles of kPrefillBM rows, and each group's blob address (pool lookup for
-// routed experts with at least one token).
-__global__ void __launch_bounds__(1024) k_prefill_setup(const int32_t* __restrict__ counts,
-                                                         const int32_t* __restrict__ offsets,
-                                                         int E, int T, int K, int S,
-                                                         ExpertSource src,
-                                                         const uint8_t* shared_blob,
-                                                         int32_t* __restrict__ gstart,
-                                                         int32_t* __restrict__ tstart,
-                                                         unsigned long long* __restrict__ gblob,
-                                                         uint32_t* __restrict__ hmax, int NR) {
-  __shared__ int lds16[16];
-  const int e = threadIdx.x;
-  for (int i = e; i < NR; i += 1024) hmax[i] = 0u;  // row maxima of the gate/up epilogue
-  const int n = (e < E) ? counts[e] : 0;
-  const int tiles = (n + kPrefillBM - 1) / kPrefillBM;
-  int total;
-  const int ts = block_exclusive_scan_1024(tiles, lds16, total);
-  if (e < E) {
-    gstart[e] = offsets[e];
-    tstart[e] = ts;
-    const uint8_t* b;
-    if (src.expert_to_slot == nullptr) {
-      b = src.slots + size_t(e) * src.stride;
-    } else {
-      const int slot = src.expert_to_slot[e];
-      if (n > 0 && src.counters) {
-        atomicAdd(&src.counters[1], 1ull);
-        if (slot >= 0) atomicAdd(&src.counters[0], 1ull);
-      }
-      b = slot >= 0 ? src.slots + size_t(slot) * src.stride : src.host_blobs + size_t(e) * src.stride;
-    }
-    gblob[e] = reinterpret_cast<unsigned long long>(b);
-  }
-  if (e == 0) {
-    const int TK = T * K;
-    gstart[E] = TK;
-    gstart[E + 1] = TK + S * T;
-    tstart[E] = total;
-    tstart[E + 1] = total + S * ((T + kPrefillBM - 1) / kPrefillBM);
-    gblob[E] = reinterpret_cast<unsigned long long>(shared_blob);
-  }
-}
-
 // ===========================================================================
 // grouped GEMM
 // ===========================================================================
@@ -455,7 +410,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
           const int n = n0 + wn0 + 16 * j + (lane & 15);
           const float v = acc[i][j][q];
           if (MODE == kRouter) {
-            if (a.plog) {  // partial of this K split; summed (and biased) by k_router_reduce
+            if (a.plog) {  // partial of this K split; summed (and biased) by the top-K kernel
               if (n < Nrows) a.plog[(size_t(ks) * a.T + s) * Nrows + n] = v;
             } else if (n < a.E) {
               a.logits[size_t(s) * a.E + n] = v + (a.bias ? a.bias[n] : 0.f);
@@ -501,22 +456,6 @@ hipError_t launch_group(const int32_t* idx, int T, int K, int E, int32_t* counts
 
 constexpr int kLoraBM = 64;  // rows per LoRA-A workgroup (two per group tile)
 
-// logits[t][e] = sum over the K splits (in split order) + bias[e]; column E
-// (the shared-gate logit) goes to sg_logit.  grid ceil(T * (E + S) / 256).
-__global__ void __launch_bounds__(256) k_router_reduce(const float* __restrict__ plog, int nks, int T,
-                                                       int E, int S, const float* __restrict__ bias,
-                                                       float* __restrict__ logits,
-                                                       float* __restrict__ sg_logit) {
-  const int N = E + S;
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= T * N) return;
-  const int t = i / N, n = i % N;
-  float v = 0.f;
-  for (int k = 0; k < nks; ++k) v += plog[(size_t(k) * T + t) * N + n];
-  if (n < E) logits[size_t(t) * E + n] = v + (bias ? bias[n] : 0.f);
-  else sg_logit[t] = v;
-}
-
 // u[s] of the gate/up LoRA chunk from the K-split partials of A_gate x and
 // A_up x (columns 0..15 and 16..31): lambda * (A v) * 2^-ex[token], as
 // [gate hi 0..15 | gate lo 16..31 | up hi 32..47 | up lo 48..63] bf16, ranks
@@ -543,12 +482,8 @@ hipError_t launch_router_gemm(const GemmArgs& a, hipStream_t st) {
   // split K so a few thousand tokens give about 1000 workgroups with short
   // chunk loops; the partial sums are reduced in a fixed order
   const int nks = a.plog ? kRouterSplit : 1;
+  // (the top-K kernel sums the splits)
   hipLaunchKernelGGL((k_gemm<kRouter, BM, BN, 2, 2>), dim3(mtn * ntn, nks), dim3(256), 0, st, a);
-  if (a.plog) {
-    const int n = a.T * (a.E + a.S);
-    hipLaunchKernelGGL(k_router_reduce, dim3((n + 255) / 256), dim3(256), 0, st, a.plog, nks, a.T,
-                       a.E, a.S, a.bias, a.logits, a.sg_logit);
-  }
   return hipGetLastError();
 }
 
@@ -562,11 +497,24 @@ hipError_t launch_prefill_experts(const GemmArgs& a, const int32_t* counts, Expe
                                   const uint8_t* shared_blob, uint16_t* x16, int32_t* ex,
                                   uint16_t* hs16, int32_t* eh, hipStream_t st) {
   const int NR = a.T * a.K + a.S * a.T;
-  hipLaunchKernelGGL(k_prefill_setup, dim3(1), dim3(1024), 0, st, counts, a.offsets, a.E, a.T,
-                     a.K, a.S, src, shared_blob, const_cast<int32_t*>(a.gstart),
-                     const_cast<int32_t*>(a.tstart), const_cast<unsigned long long*>(a.gblob),
-                     a.hmax, NR);
-  hipError_t e = launch_x16(a.x, a.T, a.H, x16, ex, st);
+  X16SetupArgs xs;
+  xs.x = a.x;
+  xs.T = a.T;
+  xs.H = a.H;
+  xs.E = a.E;
+  xs.K = a.K;
+  xs.S = a.S;
+  xs.x16 = x16;
+  xs.ex = ex;
+  xs.hmax = a.hmax;
+  xs.counts = counts;
+  xs.offsets = a.offsets;
+  xs.src = src;
+  xs.shared_blob = shared_blob;
+  xs.gstart = const_cast<int32_t*>(a.gstart);
+  xs.tstart = const_cast<int32_t*>(a.tstart);
+  xs.gblob = const_cast<unsigned long long*>(a.gblob);
+  hipError_t e = launch_x16_setup(xs, st);
   if (e != hipSuccess) return e;
   const int mt = prefill_max_mtiles(a.T, a.K, a.E, a.S);
   if (a.r > 0) {  // LoRA-A of gate/up: K split in kLoraSplit, partials summed in order

@@ -72,21 +72,60 @@ __global__ void __launch_bounds__(256) k_router_logits(const int8_t* __restrict_
   }
 }
 
+constexpr int kMaxTopkSplits = 4;  // K splits of the router GEMM summed by k_topk
+
 // One wave per token: K rounds of wave argmax over (logit desc, index asc),
-// then the routing weights and the shared gate.  grid ceil(T/4), block 256.
-__global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits,
-                                               const float* __restrict__ sg_logit, int T, int E,
+// then the routing weights and the shared gate.  With plog the logits are
+// first summed from the K splits of the router GEMM (split order, then the
+// bias) and stored.  grid ceil(T/4), block 256.
+__global__ void __launch_bounds__(256) k_topk(float* __restrict__ logits,
+                                               float* __restrict__ sg_logit, int T, int E,
                                                int K, int n_shared, int norm,
                                                int32_t* __restrict__ idx, float* __restrict__ w,
-                                               float* __restrict__ sw) {
+                                               float* __restrict__ sw,
+                                               const float* __restrict__ plog, int nks,
+                                               const float* __restrict__ bias) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* l = logits + size_t(t) * E;
+  float* l = logits + size_t(t) * E;
   constexpr int MP = kMaxE / 64;
   float v[MP];
 #pragma unroll
-  for (int m = 0; m < MP; ++m) v[m] = l[min(lane + 64 * m, E - 1)];  // entries >= E are not read
+  for (int m = 0; m < MP; ++m) v[m] = 0.f;
+  float sgl = 0.f;  // shared-gate logit
+  if (plog) {
+    const int N = E + n_shared;
+#pragma unroll
+    for (int m = 0; m < MP; ++m) {
+      const int n = lane + 64 * m;
+      if (64 * m >= N) break;
+      // every split's load first (clamped, unconditional), then the sum in split order
+      float pv[kMaxTopkSplits];
+#pragma unroll
+      for (int k = 0; k < kMaxTopkSplits; ++k)
+        pv[k] = plog[(size_t(min(k, nks - 1)) * T + t) * N + min(n, N - 1)];
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < kMaxTopkSplits; ++k)
+        if (k < nks) acc += pv[k];
+      if (n < E) {
+        v[m] = acc + (bias ? bias[n] : 0.f);
+        l[n] = v[m];
+      } else {
+        v[m] = 0.f;  // entries >= E are not read
+        if (n == E && n_shared) {
+          sgl = acc;
+          sg_logit[t] = acc;
+        }
+      }
+    }
+    if (n_shared) sgl = __shfl(sgl, E & 63);  // the lane that summed column E
+  } else {
+#pragma unroll
+    for (int m = 0; m < MP; ++m) v[m] = l[min(lane + 64 * m, E - 1)];  // entries >= E are not read
+    if (n_shared) sgl = sg_logit[t];
+  }
   // softmax weights over the selection (norm) or full-softmax entries
   float first = 0.f, denom = 0.f, mine = 0.f;
   int mine_e = 0;
@@ -110,7 +149,7 @@ __global__ void __launch_bounds__(256) k_topk(const float* __restrict__ logits,
     idx[size_t(t) * K + lane] = mine_e;
     w[size_t(t) * K + lane] = mine / denom;
   }
-  if (n_shared && lane == 0) sw[t] = sigmoid_f(sg_logit[t]);
+  if (n_shared && lane == 0) sw[t] = sigmoid_f(sgl);
 }
 
 // ---------------------------------------------------------------------------
@@ -144,11 +183,12 @@ hipError_t launch_router_logits(int H, const int8_t* q, const float* s, const in
 #undef MOE_CASE
 }
 
-hipError_t launch_topk(const float* logits, const float* sg_logit, int T, int E, int K,
-                       int n_shared, int norm, int32_t* idx, float* w, float* sw,
-                       hipStream_t st) {
+hipError_t launch_topk(float* logits, float* sg_logit, int T, int E, int K, int n_shared,
+                       int norm, int32_t* idx, float* w, float* sw, hipStream_t st,
+                       const float* plog, int nks, const float* bias) {
+  if (plog && (nks < 1 || nks > kMaxTopkSplits)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, sg_logit, T, E, K,
-                     n_shared, norm, idx, w, sw);
+                     n_shared, norm, idx, w, sw, plog, nks, bias);
   return hipGetLastError();
 }
 
