@@ -75,6 +75,10 @@ extern "C" moe_status_t moe_route(const moe_dims_t* d, const int8_t* gate_q, con
   float* sg = reinterpret_cast<float*>(wsb + W.sg);
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* plog = nullptr;  // K-split partial logits, summed by the top-K kernel
+  // grouping: per-chunk expert histograms, zeroed by the router kernel and
+  // filled by the top-K kernel
+  int32_t* hist = group ? reinterpret_cast<int32_t*>(wsb + W.chunk_hist) : nullptr;
+  const int nhist = group ? ((T * d->K + kGroupChunk - 1) / kGroupChunk) * d->E : 0;
   if (T >= kRouterGemmMinT) {
     // many tokens: MFMA GEMM over int8 codes (exact in bf16), fp32 group
     // scale applied per 64-column chunk
@@ -94,20 +98,20 @@ extern "C" moe_status_t moe_route(const moe_dims_t* d, const int8_t* gate_q, con
     g.logits = lg;
     g.sg_logit = sg;
     g.plog = plog = reinterpret_cast<float*>(wsb + W.plog);
+    g.zero = hist;
+    g.nzero = nhist;
     st = hip_status(launch_router_gemm(g, s), fn);
   } else {
     st = hip_status(launch_router_logits(d->H, gate_q, gate_s, sgate_q, sgate_s, x, logit_bias,
-                                         d->E, d->n_shared, T, lg, sg, s),
+                                         d->E, d->n_shared, T, lg, sg, s, hist, nhist),
                     fn);
   }
   if (st != MOE_OK) return st;
   st = hip_status(launch_topk(lg, sg, T, d->E, d->K, d->n_shared, d->norm_topk, topk_idx, topk_w,
-                              shared_w, s, plog, plog ? kRouterSplit : 0, logit_bias),
+                              shared_w, s, plog, plog ? kRouterSplit : 0, logit_bias, hist),
                   fn);
   if (st != MOE_OK || !group) return st;
-  return hip_status(launch_group(topk_idx, T, d->K, d->E, counts, offsets, perm,
-                                 reinterpret_cast<int32_t*>(wsb + W.chunk_hist),
-                                 reinterpret_cast<int32_t*>(wsb + W.base), s),
+  return hip_status(launch_group(topk_idx, T, d->K, d->E, counts, offsets, perm, hist, s),
                     fn);
 }
 

@@ -19,14 +19,17 @@ inline bool width_supported(int v) {
 hipError_t launch_router_logits(int H, const int8_t* q, const float* s, const int8_t* sq,
                                 const float* ss, const uint16_t* x, const float* bias, int E,
                                 int n_shared, int T, float* logits, float* sg_logit,
-                                hipStream_t st);
+                                hipStream_t st, int32_t* zero = nullptr, int nzero = 0);
 // Top-K, routing weights and shared gate, one wave per token.  With `plog`
 // ([nks][T][E + n_shared] partial logits of a K-split router GEMM) the wave
 // first sums the partials in split order, adds `bias` and stores the logits
-// (`logits`, `sg_logit`); otherwise it reads them.
+// (`logits`, `sg_logit`); otherwise it reads them.  With `hist` (zeroed
+// [ceil(T K / 1024)][E]) it also counts each (token, slot) pair in its
+// chunk's expert histogram for the grouping.
 hipError_t launch_topk(float* logits, float* sg_logit, int T, int E, int K, int n_shared,
                        int norm, int32_t* idx, float* w, float* sw, hipStream_t st,
-                       const float* plog = nullptr, int nks = 0, const float* bias = nullptr);
+                       const float* plog = nullptr, int nks = 0, const float* bias = nullptr,
+                       int32_t* hist = nullptr);
 
 // decode expert path
 struct DecodeArgs {

@@ -50,12 +50,14 @@ struct GemmArgs {
   float* sg_logit;
   float* plog;  // [kRouterSplit][T][E + S] partial logits of the K splits, or null (no split)
   float* upart;  // [kLoraSplit][NR][32] partial LoRA-A of gate/up over the K splits
+  int32_t* zero;  // router GEMM: nzero ints its first workgroup sets to 0 (grouping histogram)
+  int nzero;
   // down output, [T][K+S][H]
   float* y;
 };
 
 hipError_t launch_group(const int32_t* idx, int T, int K, int E, int32_t* counts,
-                        int32_t* offsets, int32_t* perm, int32_t* chunk_hist, int32_t* base,
+                        int32_t* offsets, int32_t* perm, const int32_t* chunk_hist,
                         hipStream_t st);
 hipError_t launch_router_gemm(const GemmArgs& a, hipStream_t st);
 int prefill_max_mtiles(int T, int K, int E, int S);

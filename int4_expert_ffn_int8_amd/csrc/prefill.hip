@@ -41,19 +41,6 @@ __device__ __forceinline__ unsigned long long same_key_mask(int key, int nbits, 
   return m;
 }
 
-// Per chunk of kGroupChunk pairs: histogram of experts.  grid nch, block 1024.
-__global__ void __launch_bounds__(1024) k_group_hist(const int32_t* __restrict__ idx, int TK, int E,
-                                                      int32_t* __restrict__ chunk_hist) {
-  __shared__ int h[kMaxE];
-  const int tid = threadIdx.x, c = blockIdx.x;
-  for (int e = tid; e < E; e += 1024) h[e] = 0;
-  __syncthreads();
-  const int p = c * kGroupChunk + tid;
-  if (p < TK) atomicAdd(&h[idx[p]], 1);
-  __syncthreads();
-  for (int e = tid; e < E; e += 1024) chunk_hist[size_t(c) * E + e] = h[e];
-}
-
 // Block-wide exclusive scan of one int per thread (1024 threads); returns the
 // exclusive prefix, `total` receives the sum.
 __device__ __forceinline__ int block_exclusive_scan_1024(int v, int* lds16, int& total) {
@@ -77,40 +64,40 @@ __device__ __forceinline__ int block_exclusive_scan_1024(int v, int* lds16, int&
   return wbase + inc - v;
 }
 
-// One workgroup: per-expert counts, exclusive offsets and per-chunk bases.
-__global__ void __launch_bounds__(1024) k_group_scan(const int32_t* __restrict__ chunk_hist,
-                                                      int nch, int E, int TK,
-                                                      int32_t* __restrict__ counts,
-                                                      int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ base) {
+// Stable scatter: pair p of chunk c goes to offsets[e] + (pairs of expert e in
+// chunks before c) + (earlier pairs of e in chunk c).  Every workgroup first
+// scans the per-chunk histograms (filled by the top-K kernel) for its own
+// bases and the offsets; workgroup 0 also writes counts and offsets.
+// grid nch, block 1024, dynamic LDS 16 * E ints.
+__global__ void __launch_bounds__(1024) k_group_scatter(const int32_t* __restrict__ idx, int TK,
+                                                         int E, int nbits, int nch,
+                                                         const int32_t* __restrict__ chunk_hist,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ perm) {
+  extern __shared__ int wcnt[];  // [16][E]
   __shared__ int lds16[16];
-  const int e = threadIdx.x;
-  int run = 0;
-  if (e < E) {
-    for (int c = 0; c < nch; ++c) {
-      const int v = chunk_hist[size_t(c) * E + e];
-      base[size_t(c) * E + e] = run;
-      run += v;
+  __shared__ int lds_start[kMaxE];  // offsets[e] + pairs of e in earlier chunks
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = blockIdx.x;
+  // bases of this chunk and the totals, for expert tid
+  int before = 0, tot = 0;
+  if (tid < E) {
+    for (int cc = 0; cc < nch; ++cc) {
+      const int v = chunk_hist[size_t(cc) * E + tid];
+      before += (cc < c) ? v : 0;
+      tot += v;
     }
   }
   int total;
-  const int off = block_exclusive_scan_1024(e < E ? run : 0, lds16, total);
-  if (e < E) {
-    counts[e] = run;
-    offsets[e] = off;
+  const int off = block_exclusive_scan_1024(tid < E ? tot : 0, lds16, total);
+  if (tid < E) {
+    lds_start[tid] = off + before;
+    if (c == 0) {
+      counts[tid] = tot;
+      offsets[tid] = off;
+    }
   }
-  if (e == 0) offsets[E] = TK;
-}
-
-// Stable scatter: pair p goes to offsets[e] + (earlier pairs of expert e).
-// grid nch, block 1024, dynamic LDS 16 * E ints.
-__global__ void __launch_bounds__(1024) k_group_scatter(const int32_t* __restrict__ idx, int TK,
-                                                         int E, int nbits,
-                                                         const int32_t* __restrict__ offsets,
-                                                         const int32_t* __restrict__ base,
-                                                         int32_t* __restrict__ perm) {
-  extern __shared__ int wcnt[];  // [16][E]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = blockIdx.x;
+  if (c == 0 && tid == 0) offsets[E] = TK;
   for (int i = tid; i < 16 * E; i += 1024) wcnt[i] = 0;
   __syncthreads();
   const int p = c * kGroupChunk + tid;
@@ -123,7 +110,7 @@ __global__ void __launch_bounds__(1024) k_group_scatter(const int32_t* __restric
   if (valid) {
     int pre = 0;
     for (int w = 0; w < wave; ++w) pre += wcnt[w * E + e];
-    perm[offsets[e] + base[size_t(c) * E + e] + pre + rank] = p;
+    perm[lds_start[e] + pre + rank] = p;
   }
 }
 
@@ -186,6 +173,8 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDS_STRIDE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave / WN) * C::WTM, wn0 = (wave % WN) * C::WTN;
+  if (MODE == kRouter && a.zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = tid; i < a.nzero; i += 256) a.zero[i] = 0;
 
   // ---- which tile ---------------------------------------------------------
   int ntn, Kdim, Nrows;
@@ -439,18 +428,15 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
 // host launchers
 // ===========================================================================
 hipError_t launch_group(const int32_t* idx, int T, int K, int E, int32_t* counts,
-                        int32_t* offsets, int32_t* perm, int32_t* chunk_hist, int32_t* base,
+                        int32_t* offsets, int32_t* perm, const int32_t* chunk_hist,
                         hipStream_t st) {
   const int TK = T * K;
   const int nch = (TK + kGroupChunk - 1) / kGroupChunk;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  if (nch > 0) hipLaunchKernelGGL(k_group_hist, dim3(nch), dim3(1024), 0, st, idx, TK, E, chunk_hist);
-  hipLaunchKernelGGL(k_group_scan, dim3(1), dim3(1024), 0, st, chunk_hist, nch, E, TK, counts,
-                     offsets, base);
   if (nch > 0)
     hipLaunchKernelGGL(k_group_scatter, dim3(nch), dim3(1024), 16 * E * sizeof(int), st, idx, TK,
-                       E, nbits, offsets, base, perm);
+                       E, nbits, nch, chunk_hist, counts, offsets, perm);
   return hipGetLastError();
 }
 

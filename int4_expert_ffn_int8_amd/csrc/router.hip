@@ -7,6 +7,7 @@
 #include "device_utils.h"
 #include "launch.h"
 #include "moe_internal.h"
+#include "prefill.h"
 #include "topk.h"
 
 namespace moe {
@@ -23,8 +24,11 @@ __global__ void __launch_bounds__(256) k_router_logits(const int8_t* __restrict_
                                                         const uint16_t* __restrict__ x,
                                                         const float* __restrict__ bias, int E,
                                                         int n_shared, float* __restrict__ logits,
-                                                        float* __restrict__ sg_logit) {
+                                                        float* __restrict__ sg_logit,
+                                                        int32_t* __restrict__ zero, int nzero) {
   using G = Geo<H>;
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0)  // the grouping histogram
+    for (int i = threadIdx.x; i < nzero; i += 256) zero[i] = 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % G::LPR;
   const int t = blockIdx.y;
@@ -84,7 +88,8 @@ __global__ void __launch_bounds__(256) k_topk(float* __restrict__ logits,
                                                int32_t* __restrict__ idx, float* __restrict__ w,
                                                float* __restrict__ sw,
                                                const float* __restrict__ plog, int nks,
-                                               const float* __restrict__ bias) {
+                                               const float* __restrict__ bias,
+                                               int32_t* __restrict__ hist) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -148,6 +153,9 @@ __global__ void __launch_bounds__(256) k_topk(float* __restrict__ logits,
   if (lane < K) {
     idx[size_t(t) * K + lane] = mine_e;
     w[size_t(t) * K + lane] = mine / denom;
+    // per-chunk expert histogram of the (token, slot) pairs for the grouping
+    // (integer adds: the counts do not depend on their order)
+    if (hist) atomicAdd(&hist[size_t((t * K + lane) / kGroupChunk) * E + mine_e], 1);
   }
   if (n_shared && lane == 0) sw[t] = sigmoid_f(sgl);
 }
@@ -159,22 +167,24 @@ template <int H>
 static hipError_t launch_router_logits_t(const int8_t* q, const float* s, const int8_t* sq,
                                          const float* ss, const uint16_t* x, const float* bias,
                                          int E, int n_shared, int T, float* logits,
-                                         float* sg_logit, hipStream_t st) {
+                                         float* sg_logit, hipStream_t st, int32_t* zero,
+                                         int nzero) {
   using G = Geo<H>;
   const int rows = E + n_shared;
   dim3 grid((rows + 4 * G::RPL - 1) / (4 * G::RPL), T);
   hipLaunchKernelGGL(k_router_logits<H>, grid, dim3(256), 0, st, q, s, sq, ss, x, bias, E,
-                     n_shared, logits, sg_logit);
+                     n_shared, logits, sg_logit, zero, nzero);
   return hipGetLastError();
 }
 
 hipError_t launch_router_logits(int H, const int8_t* q, const float* s, const int8_t* sq,
                                 const float* ss, const uint16_t* x, const float* bias, int E,
                                 int n_shared, int T, float* logits, float* sg_logit,
-                                hipStream_t st) {
+                                hipStream_t st, int32_t* zero, int nzero) {
 #define MOE_CASE(V) \
   case V:           \
-    return launch_router_logits_t<V>(q, s, sq, ss, x, bias, E, n_shared, T, logits, sg_logit, st);
+    return launch_router_logits_t<V>(q, s, sq, ss, x, bias, E, n_shared, T, logits, sg_logit, st, \
+                                     zero, nzero);
   switch (H) {
     MOE_FOR_EACH_WIDTH(MOE_CASE)
     default:
@@ -185,10 +195,10 @@ hipError_t launch_router_logits(int H, const int8_t* q, const float* s, const in
 
 hipError_t launch_topk(float* logits, float* sg_logit, int T, int E, int K, int n_shared,
                        int norm, int32_t* idx, float* w, float* sw, hipStream_t st,
-                       const float* plog, int nks, const float* bias) {
+                       const float* plog, int nks, const float* bias, int32_t* hist) {
   if (plog && (nks < 1 || nks > kMaxTopkSplits)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, sg_logit, T, E, K,
-                     n_shared, norm, idx, w, sw, plog, nks, bias);
+                     n_shared, norm, idx, w, sw, plog, nks, bias, hist);
   return hipGetLastError();
 }
 

@@ -20,7 +20,6 @@ struct WsLayout {
   size_t vpart;    // fp32 [NP, I/JW, r]
   // prefill grouping and grouped GEMMs (NR = T*K + n_shared*T sorted rows)
   size_t chunk_hist;  // int32 [nch, E]
-  size_t base;        // int32 [nch, E]
   size_t gstart;      // int32 [E+2]
   size_t tstart;      // int32 [E+2]
   size_t gblob;       // u64 [E+1]
@@ -54,7 +53,6 @@ inline WsLayout ws_layout(const moe_dims_t& d, int T, bool prefill) {
   const size_t NR = prefill ? TK + size_t(d.n_shared) * T : 0;
   const size_t E = prefill ? d.E : 0;
   W.chunk_hist = o; o = align256(o + nch * E * 4);
-  W.base = o;       o = align256(o + nch * E * 4);
   W.gstart = o;     o = align256(o + (prefill ? (E + 2) * 4 : 0));
   W.tstart = o;     o = align256(o + (prefill ? (E + 2) * 4 : 0));
   W.gblob = o;      o = align256(o + (prefill ? (E + 1) * 8 : 0));
