@@ -116,6 +116,17 @@ def test_prefill_no_shared_k8_no_lora():
     _run_prefill(w, L, router, experts, shared, synth.tokens(w, 0, T=150), max_near_ties=2)
 
 
+@pytest.mark.parametrize("T", [40, 700])
+def test_prefill_k6_e200_pairs_straddle_histogram_chunks(T):
+    # K = 6 does not divide the 1024-pair histogram chunks, so at T = 700 the
+    # pairs of token 170 fall in two chunks; E = 200 is not a multiple of 64.
+    # T = 40 takes the GEMV router, T = 700 the MFMA router GEMM.
+    w = synth.workload(0, H=256, E=200, K=6, I=128, r=4, n_shared=1)
+    L, router, experts, shared = _layer(w, seed=11)
+    _run_prefill(w, L, router, experts, shared, synth.tokens(w, 3, T=T, seed=11),
+                 max_near_ties=2)
+
+
 def test_prefill_fewer_pairs_than_experts():
     w = synth.workload(1)
     L, router, experts, shared = _layer(w)
