@@ -92,6 +92,34 @@ def test_expert_forward_validation(B):
     assert st == 1 and b"shared_blob" in B.load().moe_last_error()
 
 
+def test_block_decode_exec_and_read_delay_validation(B):
+    # checked on the host before any launch: a NULL exec_idx, and a modeled
+    # read latency above MOE_MAX_READ_DELAY_NS (1 ms)
+    d = B.dims(2048, 512, 256, 4, 16, 1)
+    fake = 1 << 40
+    lib = B.load()
+    tab = B.experts_struct(fake, 64, expert_to_slot=fake, host_blobs=fake)
+    st = lib.moe_block_decode_exec(B.ctypes.byref(d), fake, fake, fake, fake, B.ctypes.byref(tab),
+                                   fake, fake, 1, 0, 0.0, None, None, None, fake, fake, 1 << 30, 0)
+    assert st == 1 and b"exec_idx" in lib.moe_last_error()
+    slow = B.experts_struct(fake, 64, expert_to_slot=fake, host_blobs=fake,
+                            read_delay_ns=1_000_001)
+    for call in ("moe_block_decode", "moe_block_decode_exec"):
+        args = [B.ctypes.byref(d), fake, fake, fake, fake, B.ctypes.byref(slow), fake, fake, 1, 0,
+                0.0]
+        if call == "moe_block_decode_exec":
+            args.append(fake)
+        args += [None, None, fake, fake, 1 << 30, 0]
+        st = getattr(lib, call)(*args)
+        assert st == 1 and b"read_delay_ns" in lib.moe_last_error(), call
+    # T == 0 with no exec_idx is a no-op
+    ok = B.experts_struct(fake, 256)
+    assert lib.moe_block_decode_exec(B.ctypes.byref(d), fake, fake, fake, fake, B.ctypes.byref(ok),
+                                     fake, fake, 0, 0, 0.0, None, None, None, fake, fake, 1 << 30,
+                                     0) == 0
+    assert lib.moe_pool_set_read_delay(None, 0) == 1
+
+
 def test_prerouter_validation(B):
     fake = 1 << 40
     assert B.load().prerouter_predict(fake, fake, 2048, 256, 256, 0, fake, 1, fake, None, fake,
