@@ -174,12 +174,14 @@ class MoeStack:
     shared_blobs: device uint8 [L, blob] or None; routed: device uint8
     [L, E, blob] (all resident) or None with `host_blobs` (pinned uint8
     [L, E, blob]) and `pool_slots`; prerouter: per-layer (W1, W2) device bf16
-    for layers 0 .. L-2, or None.
+    for layers 0 .. L-2, or None.  With prerouter_feat, W1 is [D, H + E] and
+    each head also sees the experts its layer executed (routing features,
+    [P2] Prerouter paragraph).
     """
 
     def __init__(self, H, I, E, K, r, n_shared, lora_scale, routers, shared_blobs, routed=None,
                  host_blobs=None, pool_slots=0, prerouter=None, pred_k=0, eps=1e-6,
-                 max_fills=-1, exec_mode="router", device="cuda"):
+                 max_fills=-1, exec_mode="router", prerouter_feat=False, device="cuda"):
         self.H, self.I, self.E, self.K, self.r, self.S = H, I, E, K, r, n_shared
         self.L = len(routers)
         self.d = B.dims(H, I, E, K, r, n_shared, lora_scale, 1)
@@ -205,6 +207,7 @@ class MoeStack:
                                   host_blobs)
             self.experts = [self.pool.layer(l, self.counters[l]) for l in range(self.L)]
         self.prerouter = prerouter
+        self.prerouter_feat = prerouter_feat
         self.pred_k = pred_k
         self.exec_mode = "router"
         self.have_pred = False
@@ -268,8 +271,13 @@ class MoeStack:
             self.layer_forward(l, cur, out, stream)
             if self.prerouter is not None and l + 1 < self.L:
                 W1, W2 = self.prerouter[l]
-                B.prerouter_predict(W1, W2, self.H, W1.shape[0], self.E, self.pred_k, out, 1,
-                                    self.pred[l + 1], None, self.pr_ws, stream)
+                if self.prerouter_feat:  # h plus the one-hot of this layer's executed experts
+                    B.prerouter_predict_feat(W1, W2, self.H, W1.shape[0], self.E, self.pred_k, out,
+                                             self.idx[l], self.K, 1, self.pred[l + 1], None,
+                                             self.pr_ws, stream)
+                else:
+                    B.prerouter_predict(W1, W2, self.H, W1.shape[0], self.E, self.pred_k, out, 1,
+                                        self.pred[l + 1], None, self.pr_ws, stream)
             cur = out
         if self.exec_mode == "predict":
             # this step's predictions are the next step's routes

@@ -11,6 +11,8 @@
   against the oracle's stack layer with the executed experts given, and
   after the first step every lookup of layers 1 .. L-1 is served from a
   slot (the layer waited for its fills).
+* The same with routing-feature heads: each head also sees the experts its
+  layer executed; its predictions are checked against the oracle's head.
 """
 import numpy as np
 import pytest
@@ -171,3 +173,50 @@ def test_predict_mode_stack_pool_resident_and_oracle():
     np.testing.assert_array_equal(c[1:, 0], c[1:, 1])
     for st in (pooled, delayed):
         st.pool.sync(st.side)
+
+
+def test_predict_mode_with_feature_heads():
+    from int4_expert_ffn_int8_amd.layer import MoeStack, dev
+    w = synth.workload(0, prerouter_D=64)
+    nl, slots, steps, K, E = 3, 4, 5, w["K"], w["E"]
+    routers, experts, shared, blobs, shared_dev = _stack_weights(w, nl)
+    ptf = [synth.prerouter_feat_tensors(w, l) for l in range(nl - 1)]
+    heads = [(dev(p["W1"]), dev(p["W2"])) for p in ptf]
+    host = torch.from_numpy(blobs).pin_memory()
+
+    def make(**kw):
+        return MoeStack(w["H"], w["I"], E, K, w["r"], w["n_shared"], w["lora_scale"], routers,
+                        shared_dev, prerouter=heads, pred_k=K, eps=1e-6, exec_mode="predict",
+                        prerouter_feat=True, **kw)
+
+    resident = make(routed=dev(blobs))
+    pooled = make(host_blobs=host, pool_slots=slots)
+    layer_outs = [torch.empty((1, w["H"]), dtype=torch.int16, device="cuda") for _ in range(nl)]
+    prev_pred = None
+    checked = 0
+    for step in range(steps):
+        print(f"predict+features step {step}", flush=True)
+        x = dev(synth.tokens(w, 400 + step))
+        o_r = resident.step(x, outs=layer_outs)
+        resident.end_step()
+        o_p = pooled.step(x)
+        pooled.end_step()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(_bits(o_p), _bits(o_r), err_msg=f"step {step}")
+        idx = resident.idx.cpu().numpy().reshape(nl, K)
+        np.testing.assert_array_equal(pooled.idx.cpu().numpy().reshape(nl, K), idx)
+        if prev_pred is not None:
+            np.testing.assert_array_equal(idx[1:], prev_pred[1:])
+        pred = resident.pred.cpu().numpy().reshape(nl, K)
+        # each head: oracle on the GPU's layer output and executed experts
+        for l in range(nl - 1):
+            h = _bits(layer_outs[l])
+            _, z_ref = O.prerouter_feat(ptf[l]["W1"], ptf[l]["W2"], h, idx[l][None, :], K)
+            order = np.lexsort((np.arange(E), -z_ref[0]))
+            margin = z_ref[0, order[K - 1]] - z_ref[0, order[K]]
+            if margin > 1e-3 * np.abs(z_ref).max():
+                assert pred[l + 1].tolist() == order[:K].tolist(), (step, l)
+                checked += 1
+        prev_pred = pred.copy()
+    assert checked >= (nl - 1) * steps // 2
+    pooled.pool.sync(pooled.side)
