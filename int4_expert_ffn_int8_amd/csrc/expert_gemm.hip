@@ -4,25 +4,27 @@
 // computes in batches over whole layers.  Per expert group the contraction is
 // dense, so it runs on v_mfma_f32_16x16x32_f16 with fp32 accumulation:
 //
-//   * weights: int4 codes are dequantised into LDS as fp16 w = s*q + b
+//   * weights: the int4 codes and the group scale/bias go through LDS; each
+//     wave dequantises its own columns in registers to fp16 w = s*q + b
 //     (affine, group 64: [P3] "iPhone、Mac、Android、Windows 实测横评…",
-//     "三件套" bullets), one rounding of the exact value (2^-11 relative),
-//     so no per-group work remains after the MFMA;
+//     "三件套" bullets), one rounding of the exact value (2^-11 relative);
 //   * activations: each row enters as fp16(v * 2^-e) with a power-of-two
 //     exponent per row chosen so the row's largest magnitude lies in
 //     [2^14, 2^15); the epilogue multiplies the row by 2^e.  Rows of x are
-//     converted once per token (k_x16), rows of the SwiGLU output h once per
-//     row after the gate/up GEMM (k_h16, from an fp32 h and its row maximum);
+//     converted once per token (k_x16_setup, whose last workgroup also does
+//     the per-group setup), rows of the SwiGLU output h once per row after
+//     the gate/up GEMM (k_h16, from an fp32 h and its row maximum);
 //   * the unmerged LoRA delta ([P1] Recover-LoRA paragraph) is one extra
 //     64-wide K chunk on bf16 MFMA: the activation side holds
 //     lambda * (A v) * 2^-e as a bf16 hi + lo pair, the weight side holds B
 //     twice.
 //
-// Tiles of 128 rows x 128 columns, 4 waves of 64 x 64, K chunks of 64 (one
-// quantisation group), LDS double-buffered with one barrier per chunk.
-// Workgroups are renumbered so that the column tiles of one row tile (which
-// share activation rows) and neighbouring row tiles of one expert (which
-// share weights) run on the same XCD and its L2.
+// Tiles of 128 rows x 256 columns per workgroup of 8 waves (each wave all 128
+// rows and 32 columns), K chunks of 64 (one quantisation group) through a
+// ring of three LDS stages filled by LDS DMA two chunks ahead; two
+// workgroups per CU.  Workgroups are renumbered so that the column tiles of
+// one row tile (which share activation rows) and neighbouring row tiles of
+// one expert (which share weights) run on the same XCD and its L2.
 #include "device_utils.h"
 #include "launch.h"
 #include "moe_internal.h"

@@ -4,8 +4,9 @@
 // loads whole layers and computes in batches, decode relies on caching and
 // prefetch.  Here prefill groups each expert's tokens (stable, by expert) and
 // runs one dense contraction per expert (the expert GEMMs are in
-// expert_gemm.hip).  This file holds the grouping kernels, the expert-GEMM
-// setup, and k_gemm for the router GEMM (int8 codes exact in bf16, fp32
+// expert_gemm.hip).  This file holds the stable scatter of the grouping (the
+// per-chunk histograms are filled by the top-K kernel), and k_gemm for the
+// router GEMM (int8 codes exact in bf16, fp32
 // scale per 64-column chunk) and the two skinny LoRA-A GEMMs of the unmerged
 // delta ([P1] Recover-LoRA paragraph), whose outputs lambda * (A v) are
 // stored as bf16 hi + lo pairs in the row-scaled domain of the expert GEMMs.
