@@ -10,6 +10,9 @@
 //             redundantly and identically in every workgroup); the last
 //             router workgroup also waits for every logit and runs the
 //             wavefront top-K, publishing ids, weights and the shared gate.
+//             With given experts (prediction-as-routing, [P3] "三件套"
+//             Prerouter bullet) it publishes those instead, weighted by the
+//             softmax of their logits.
 //   lora_a    u = [A_gate; A_up] x for one (token, slot) pair.
 //   gate_up   32 gate/up outputs of one pair (+ lambda B u), SwiGLU -> h
 //             (fp16), and that block's partial of v = A_down h.
@@ -18,7 +21,9 @@
 //             then the weighted combine (+ residual) -> out.
 //
 // Weight loads are issued before the waits they do not depend on (shared
-// expert from the start, routed experts as soon as their ids arrive).  A role
+// expert from the start, routed experts as soon as their ids arrive).  An
+// expert that is not resident in the pool is read from the pinned host copy,
+// after an optional modeled storage latency (a bounded wall-clock wait).  A role
 // waits only on roles with lower workgroup ids, which the dispatcher starts
 // first, and every wait is bounded: on timeout the kernel records an error
 // and still runs to completion.
