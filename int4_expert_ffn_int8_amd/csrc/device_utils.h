@@ -116,15 +116,27 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Wave-wide max / min; the result is wave-uniform.
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f<kDppXor1>(v));
-  v = fmaxf(v, dpp_f<kDppXor2>(v));
-  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp_f<kDppMirror>(v));
-  v = fmaxf(v, dpp_f<kDppBcast15, 0xA>(v, v));
-  v = fmaxf(v, dpp_f<kDppBcast31, 0xC>(v, v));
-  return readlane_f(v, 63);
+// Wave-wide max / min; the result is wave-uniform.  The float max runs on
+// order-preserving unsigned keys (sign bit set for x >= +0, all bits flipped
+// for negatives), an exact integer max that folds into the DPP instructions;
+// it returns the largest element's bits (+0 over -0; a NaN ranks above
+// +infinity, so callers map NaN first where that matters).
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ float wave_max(float f) {
+  uint32_t v = f32_order_key(f);
+  v = max(v, dpp_u<kDppXor1>(v));
+  v = max(v, dpp_u<kDppXor2>(v));
+  v = max(v, dpp_u<kDppHalfMirror>(v));
+  v = max(v, dpp_u<kDppMirror>(v));
+  v = max(v, dpp_u<kDppBcast15, 0xA>(v, v));
+  v = max(v, dpp_u<kDppBcast31, 0xC>(v, v));
+  return f32_from_order_key(uint32_t(__builtin_amdgcn_readlane(int(v), 63)));
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   v = min(v, dpp_u<kDppXor1>(v));

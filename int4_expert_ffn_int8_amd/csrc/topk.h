@@ -4,7 +4,8 @@
 // the E routed experts, those with the largest gate logits.  Here lane l of a
 // wave holds the logits of experts l, l + 64, ...; experts are taken in order
 // of logit (descending), equal logits by expert index (ascending), which makes
-// the selection unique.
+// the selection unique.  A NaN logit ranks as -infinity, so every selection
+// is K distinct experts in [0, E) whatever the input.
 #pragma once
 
 #include "device_utils.h"
@@ -31,7 +32,7 @@ __device__ __forceinline__ void topk_wave_sorted(const float* vin, int E, int K,
   for (int m = 0; m < MP; ++m) {
     const uint32_t idx = uint32_t(lane + 64 * m);
     const bool ok = idx < uint32_t(E);
-    v[m] = ok ? vin[m] : -INFINITY;
+    v[m] = (ok && !isnan(vin[m])) ? vin[m] : -INFINITY;
     e[m] = ok ? idx : kNoExpert;
   }
 #pragma unroll
@@ -73,11 +74,13 @@ __device__ __forceinline__ void topk_wave_scan(const float* vin, int E, int K, i
     float bv = -INFINITY;
     uint32_t be = kNoExpert;
 #pragma unroll
-    for (int m = 0; m < MP; ++m)  // ascending index keeps the lowest among equal logits
-      if (64 * m < E && ((alive >> m) & 1) && (be == kNoExpert || vin[m] > bv)) {
-        bv = vin[m];
+    for (int m = 0; m < MP; ++m) {  // ascending index keeps the lowest among equal logits
+      const float x = isnan(vin[m]) ? -INFINITY : vin[m];
+      if (64 * m < E && ((alive >> m) & 1) && (be == kNoExpert || x > bv)) {
+        bv = x;
         be = uint32_t(lane + 64 * m);
       }
+    }
     const float mx = wave_max(bv);
     const uint32_t sel = wave_min_u32((be != kNoExpert && bv == mx) ? be : kNoExpert);
     if ((sel & 63) == uint32_t(lane)) alive &= ~(1u << (sel >> 6));
