@@ -178,7 +178,11 @@ MOE_API moe_status_t moe_route(const moe_dims_t* d, const int8_t* gate_q, const 
  *   h = silu(a_gate(x)) * a_up(x);  y = a_down(h)   (h is rounded to bf16).
  *   routed       where the routed experts live (see moe_experts_t).
  *   shared_blob  device blob of the shared expert (n_shared == 1) or NULL.
- *   x            device bf16 [T, H];  topk_idx device int32 [T, K].
+ *   x            device bf16 [T, H];  topk_idx device int32 [T, K] (the decode
+ *                path clamps an entry outside [0, E) into range: that slot's
+ *                output is then undefined, but no address leaves the experts).
+ *                counts/offsets/perm must be moe_route's grouping outputs for
+ *                the same T, K and E.
  *   counts, offsets, perm: NULL -> decode path (weight-streaming GEMV, one
  *                pass over each selected expert per token); the outputs of
  *                moe_route's grouping -> prefill path (grouped MFMA GEMM

@@ -192,6 +192,7 @@ extern "C" moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_expert
   a.H = d->H;
   a.I = d->I;
   a.K = d->K;
+  a.E = d->E;
   a.S = d->n_shared;
   a.r = d->r;
   a.lam = d->lora_scale;

@@ -50,7 +50,8 @@ __device__ __forceinline__ const uint8_t* resolve_blob(const DecodeArgs& a, int 
   const int KS = a.K + a.S;
   const int t = p / KS, k = p % KS;
   if (k >= a.K) return a.shared_blob;
-  const int e = a.topk_idx[size_t(t) * a.K + k];
+  // a caller-supplied id outside [0, E) is clamped: never an address past the experts
+  const int e = min(max(a.topk_idx[size_t(t) * a.K + k], 0), a.E - 1);
   if (a.src.expert_to_slot == nullptr) return a.src.slots + size_t(e) * a.src.stride;
   const int slot = a.src.expert_to_slot[e];
   if (count && a.src.counters) {

@@ -34,8 +34,8 @@ hipError_t launch_topk(float* logits, float* sg_logit, int T, int E, int K, int 
 // decode expert path
 struct DecodeArgs {
   const uint16_t* x;       // [T, H]
-  const int32_t* topk_idx; // [T, K]
-  int T, H, I, K, S, r;
+  const int32_t* topk_idx; // [T, K]; entries are clamped into [0, E)
+  int T, H, I, K, S, r, E;
   float lam;
   ExpertSource src;
   const uint8_t* shared_blob;
