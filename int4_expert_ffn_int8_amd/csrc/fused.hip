@@ -188,6 +188,94 @@ __device__ __forceinline__ float slice_dot(const uint4 q, uint32_t sbw, const ui
 }
 
 // ---------------------------------------------------------------------------
+// One wave routes token t: waits for all its logits (and the shared-gate
+// logit), selects (or takes the given experts), publishes ids and weights.
+// MP logits per lane (experts lane + 64 m).
+template <int MP>
+__device__ void route_token(const FusedArgs& a, int t, int lane, unsigned tag) {
+  const tword_t* l = a.logits + t * (a.E + 1);
+  float v[MP];
+  float sgl = 0.f;
+  for (unsigned n = 0;; ++n) {
+    tword_t w[MP];
+#pragma unroll
+    for (int m = 0; m < MP; ++m) w[m] = ld_dev(&l[min(lane + 64 * m, a.E - 1)]);
+    const tword_t ws = ld_dev(&l[a.E]);  // shared-gate logit (unused without S)
+    unsigned bad = unsigned(a.S != 0) & unsigned(!has_tag(ws, tag));
+#pragma unroll
+    for (int m = 0; m < MP; ++m) {
+      bad |= unsigned(lane + 64 * m < a.E) & unsigned(!has_tag(w[m], tag));
+      v[m] = wf(w[m]);
+    }
+    sgl = wf(ws);
+    if (__all(bad == 0)) break;
+    if (++n > kFusedSpinLimit) {
+      if (lane == 0) set_err(a);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  float first = 0.f, denom = 0.f, mine = 0.f;
+  int mine_e = 0;
+  if (a.exec_idx == nullptr) {
+    topk_wave(v, a.E, a.K, lane, [&](int k, float mx, uint32_t sel) {
+      if (k == 0) first = mx;
+      const float ev = expf(mx - first);
+      denom += ev;
+      if (k == lane) {
+        mine = ev;
+        mine_e = int(sel);
+      }
+    });
+  } else {
+    // given experts: lane k < K takes expert exec_idx[t][k] and fetches its
+    // logit from the lane that holds it
+    if (lane < a.K) {
+      mine_e = a.exec_idx[t * a.K + lane];
+      if (uint32_t(mine_e) >= uint32_t(a.E)) {
+        set_err(a);
+        mine_e = 0;
+      }
+    }
+    float gl = 0.f;
+#pragma unroll
+    for (int m = 0; m < MP; ++m) {
+      if (64 * m >= a.E) break;
+      const float c = __shfl(v[m], mine_e & 63);
+      if ((mine_e >> 6) == m) gl = c;
+    }
+    first = wave_max(lane < a.K ? gl : -INFINITY);
+    mine = lane < a.K ? expf(gl - first) : 0.f;
+    // summed in k order, as the selection path does: given experts equal
+    // to the router's top-K reproduce its weights bit for bit
+    for (int k = 0; k < a.K; ++k) denom += __shfl(mine, k);
+    if (!a.norm_topk) {  // the full-softmax form below subtracts the largest logit
+      float mx = -INFINITY;
+#pragma unroll
+      for (int m = 0; m < MP; ++m)
+        if (lane + 64 * m < a.E) mx = fmaxf(mx, v[m]);
+      const float top = wave_max(mx);
+      mine = lane < a.K ? expf(gl - top) : 0.f;
+      first = top;
+    }
+  }
+  if (!a.norm_topk) {  // full-softmax entries: denominator over all E
+    float part = 0.f;
+#pragma unroll
+    for (int m = 0; m < MP; ++m)
+      if (lane + 64 * m < a.E) part += expf(v[m] - first);
+    denom = group_sum<64>(part);
+  }
+  if (lane < a.K) {
+    const float wv = mine / denom;
+    st_dev(&a.route[t * a.K + lane], tw(tag, uint32_t(mine_e)));
+    st_dev(&a.wts[t * (a.K + 1) + lane], twf(tag, wv));
+    if (a.user_idx) a.user_idx[t * a.K + lane] = mine_e;
+    if (a.user_w) a.user_w[t * a.K + lane] = wv;
+  }
+  if (a.S && lane == 0) st_dev(&a.wts[t * (a.K + 1) + a.K], twf(tag, sigmoid_f(sgl)));
+}
+
 template <int H>
 __device__ void role_router(const FusedArgs& a, int b) {
   using G = Geo<H>;
@@ -227,88 +315,10 @@ __device__ void role_router(const FusedArgs& a, int b) {
   // The last router workgroup: wait for every logit of its token (one wave
   // per token), then K rounds of wave argmax by (logit desc, index asc).
   for (int t = wave; t < a.T; t += 4) {
-    const tword_t* l = a.logits + t * (a.E + 1);
-    constexpr int MP = kMaxE / 64;
-    float v[MP];
-    float sgl = 0.f;
-    for (unsigned n = 0;; ++n) {
-      tword_t w[MP];
-#pragma unroll
-      for (int m = 0; m < MP; ++m) w[m] = ld_dev(&l[min(lane + 64 * m, a.E - 1)]);
-      const tword_t ws = ld_dev(&l[a.E]);  // shared-gate logit (unused without S)
-      unsigned bad = unsigned(a.S != 0) & unsigned(!has_tag(ws, tag));
-#pragma unroll
-      for (int m = 0; m < MP; ++m) {
-        bad |= unsigned(lane + 64 * m < a.E) & unsigned(!has_tag(w[m], tag));
-        v[m] = wf(w[m]);
-      }
-      sgl = wf(ws);
-      if (__all(bad == 0)) break;
-      if (++n > kFusedSpinLimit) {
-        if (lane == 0) set_err(a);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    float first = 0.f, denom = 0.f, mine = 0.f;
-    int mine_e = 0;
-    if (a.exec_idx == nullptr) {
-      topk_wave(v, a.E, a.K, lane, [&](int k, float mx, uint32_t sel) {
-        if (k == 0) first = mx;
-        const float ev = expf(mx - first);
-        denom += ev;
-        if (k == lane) {
-          mine = ev;
-          mine_e = int(sel);
-        }
-      });
-    } else {
-      // given experts: lane k < K takes expert exec_idx[t][k] and fetches its
-      // logit from the lane that holds it
-      if (lane < a.K) {
-        mine_e = a.exec_idx[t * a.K + lane];
-        if (uint32_t(mine_e) >= uint32_t(a.E)) {
-          set_err(a);
-          mine_e = 0;
-        }
-      }
-      float gl = 0.f;
-#pragma unroll
-      for (int m = 0; m < MP; ++m) {
-        if (64 * m >= a.E) break;
-        const float c = __shfl(v[m], mine_e & 63);
-        if ((mine_e >> 6) == m) gl = c;
-      }
-      first = wave_max(lane < a.K ? gl : -INFINITY);
-      mine = lane < a.K ? expf(gl - first) : 0.f;
-      // summed in k order, as the selection path does: given experts equal
-      // to the router's top-K reproduce its weights bit for bit
-      for (int k = 0; k < a.K; ++k) denom += __shfl(mine, k);
-      if (!a.norm_topk) {  // the full-softmax form below subtracts the largest logit
-        float mx = -INFINITY;
-#pragma unroll
-        for (int m = 0; m < MP; ++m)
-          if (lane + 64 * m < a.E) mx = fmaxf(mx, v[m]);
-        const float top = wave_max(mx);
-        mine = lane < a.K ? expf(gl - top) : 0.f;
-        first = top;
-      }
-    }
-    if (!a.norm_topk) {  // full-softmax entries: denominator over all E
-      float part = 0.f;
-#pragma unroll
-      for (int m = 0; m < MP; ++m)
-        if (lane + 64 * m < a.E) part += expf(v[m] - first);
-      denom = group_sum<64>(part);
-    }
-    if (lane < a.K) {
-      const float wv = mine / denom;
-      st_dev(&a.route[t * a.K + lane], tw(tag, uint32_t(mine_e)));
-      st_dev(&a.wts[t * (a.K + 1) + lane], twf(tag, wv));
-      if (a.user_idx) a.user_idx[t * a.K + lane] = mine_e;
-      if (a.user_w) a.user_w[t * a.K + lane] = wv;
-    }
-    if (a.S && lane == 0) st_dev(&a.wts[t * (a.K + 1) + a.K], twf(tag, sigmoid_f(sgl)));
+    if (a.E <= 256)  // four logits per lane: no loads beyond the experts
+      route_token<4>(a, t, lane, tag);
+    else
+      route_token<kMaxE / 64>(a, t, lane, tag);
   }
 }
 

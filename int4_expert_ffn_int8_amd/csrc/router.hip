@@ -81,7 +81,8 @@ constexpr int kMaxTopkSplits = 4;  // K splits of the router GEMM summed by k_to
 // One wave per token: K rounds of wave argmax over (logit desc, index asc),
 // then the routing weights and the shared gate.  With plog the logits are
 // first summed from the K splits of the router GEMM (split order, then the
-// bias) and stored.  grid ceil(T/4), block 256.
+// bias) and stored.  MP logits per lane (E <= 64 MP).  grid ceil(T/4), block 256.
+template <int MP>
 __global__ void __launch_bounds__(256) k_topk(float* __restrict__ logits,
                                                float* __restrict__ sg_logit, int T, int E,
                                                int K, int n_shared, int norm,
@@ -94,18 +95,15 @@ __global__ void __launch_bounds__(256) k_topk(float* __restrict__ logits,
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   float* l = logits + size_t(t) * E;
-  constexpr int MP = kMaxE / 64;
   float v[MP];
 #pragma unroll
   for (int m = 0; m < MP; ++m) v[m] = 0.f;
   float sgl = 0.f;  // shared-gate logit
   if (plog) {
     const int N = E + n_shared;
-#pragma unroll
-    for (int m = 0; m < MP; ++m) {
-      const int n = lane + 64 * m;
-      if (64 * m >= N) break;
-      // every split's load first (clamped, unconditional), then the sum in split order
+    // the sum of column n over the splits: every split's load first (clamped,
+    // unconditional), then the sum in split order
+    auto split_sum = [&](int n) {
       float pv[kMaxTopkSplits];
 #pragma unroll
       for (int k = 0; k < kMaxTopkSplits; ++k)
@@ -114,18 +112,22 @@ __global__ void __launch_bounds__(256) k_topk(float* __restrict__ logits,
 #pragma unroll
       for (int k = 0; k < kMaxTopkSplits; ++k)
         if (k < nks) acc += pv[k];
+      return acc;
+    };
+#pragma unroll
+    for (int m = 0; m < MP; ++m) {
+      if (64 * m >= E) break;
+      const int n = lane + 64 * m;
+      const float acc = split_sum(n);
       if (n < E) {
         v[m] = acc + (bias ? bias[n] : 0.f);
         l[n] = v[m];
-      } else {
-        v[m] = 0.f;  // entries >= E are not read
-        if (n == E && n_shared) {
-          sgl = acc;
-          sg_logit[t] = acc;
-        }
-      }
+      }  // entries >= E are not read
     }
-    if (n_shared) sgl = __shfl(sgl, E & 63);  // the lane that summed column E
+    if (n_shared) {  // column E: the shared-gate logit (every lane sums it)
+      sgl = split_sum(E);
+      if (lane == 0) sg_logit[t] = sgl;
+    }
   } else {
 #pragma unroll
     for (int m = 0; m < MP; ++m) v[m] = l[min(lane + 64 * m, E - 1)];  // entries >= E are not read
@@ -197,8 +199,12 @@ hipError_t launch_topk(float* logits, float* sg_logit, int T, int E, int K, int 
                        int norm, int32_t* idx, float* w, float* sw, hipStream_t st,
                        const float* plog, int nks, const float* bias, int32_t* hist) {
   if (plog && (nks < 1 || nks > kMaxTopkSplits)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, st, logits, sg_logit, T, E, K,
-                     n_shared, norm, idx, w, sw, plog, nks, bias, hist);
+  if (E <= 256)  // four logits per lane
+    hipLaunchKernelGGL(k_topk<4>, dim3((T + 3) / 4), dim3(256), 0, st, logits, sg_logit, T, E, K,
+                       n_shared, norm, idx, w, sw, plog, nks, bias, hist);
+  else
+    hipLaunchKernelGGL(k_topk<kMaxE / 64>, dim3((T + 3) / 4), dim3(256), 0, st, logits, sg_logit,
+                       T, E, K, n_shared, norm, idx, w, sw, plog, nks, bias, hist);
   return hipGetLastError();
 }
 
