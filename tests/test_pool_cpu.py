@@ -149,3 +149,30 @@ def test_matches_model_on_random_sequences(seed):
 def _zipf(E, rng):
     w = 1.0 / np.arange(1, E + 1) ** 1.1
     return w / w.sum()
+
+
+def test_prediction_as_routing_sequence_keeps_every_next_route_resident():
+    # In prediction-as-routing the experts executed at step s are the
+    # predictions of step s - 1, and each plan gets this step's predictions
+    # (the next routes).  With K executed + K predicted <= slots, every next
+    # route must be resident after the plan, so every lookup of the next step
+    # hits, and the executed experts of the step just finished are never
+    # evicted by it.
+    rng = np.random.default_rng(5)
+    L, E, S, K = 3, 32, 8, 3
+    lru = B.MoeLru(L, E, S)
+    prev = np.stack([rng.choice(E, K, replace=False) for _ in range(L)]).astype(np.int32)
+    lru.plan(prev, None)
+    for step in range(40):
+        nxt = np.stack([rng.choice(E, K, replace=False) for _ in range(L)]).astype(np.int32)
+        before = [lru.table(l).copy() for l in range(L)]
+        lru.plan(prev, nxt)
+        for l in range(L):
+            tab = lru.table(l)
+            assert all(tab[e] >= 0 for e in nxt[l]), (step, l)
+            # executed experts that were resident stay in their slots
+            for e in prev[l]:
+                if before[l][e] >= 0:
+                    assert tab[e] == before[l][e], (step, l, e)
+            assert len(set(tab[tab >= 0].tolist())) == int((tab >= 0).sum())  # one slot each
+        prev = nxt
