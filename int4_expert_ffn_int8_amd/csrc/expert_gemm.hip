@@ -255,16 +255,23 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t vmask, uint32_t 
 }
 
 // Eight int4 codes of one 32-bit word (columns 2s and 2s+1 in the bits
-// [4s, 4s+4) and [16+4s, 20+4s)) -> fp16 s*q + b, two per output word: the
-// code fills the low mantissa bits of fp16 1024 (0x6400), 1024 is subtracted
-// exactly and one fused multiply-add applies the group's scale and bias.
-__device__ __forceinline__ f16x8_t dequant8_fast(uint32_t w, uint32_t vmask, f16x2_t sc, f16x2_t bi) {
-  const f16x2_t off = {_Float16(1024.0f), _Float16(1024.0f)};
+// [4s, 4s+4) and [16+4s, 20+4s)) -> fp16 s*q + b, two per output word.  A
+// code in bits 0..3 of a half fills the low mantissa bits of fp16 1024
+// (0x6400, unit 1); a code in bits 4..7 those of fp16 64 (0x5400, unit 1/16),
+// so one shift by 8 serves all four positions.  The offset (1024 or 64) is
+// subtracted exactly and one fused multiply-add applies the group's scale and
+// bias.  m0 = 0x000F000F and m1 = 0x00F000F0 (in VGPRs).
+__device__ __forceinline__ f16x8_t dequant8_fast(uint32_t w, uint32_t m0, uint32_t m1, f16x2_t sc,
+                                                 f16x2_t bi) {
+  const f16x2_t off0 = {_Float16(1024.0f), _Float16(1024.0f)};
+  const f16x2_t off1 = {_Float16(64.0f), _Float16(64.0f)};
+  const uint32_t w8 = w >> 8;
+  const uint32_t c[4] = {and_or(w, m0, 0x64006400u), and_or(w, m1, 0x54005400u),
+                         and_or(w8, m0, 0x64006400u), and_or(w8, m1, 0x54005400u)};
   u32x4_t o;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const uint32_t c = and_or(s ? (w >> (4 * s)) : w, vmask, 0x64006400u);
-    const f16x2_t q = __builtin_bit_cast(f16x2_t, c) - off;  // exact
+    const f16x2_t q = __builtin_bit_cast(f16x2_t, c[s]) - ((s & 1) ? off1 : off0);  // exact
     o[s] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, sc, bi));
   }
   return __builtin_bit_cast(f16x8_t, o);
@@ -383,7 +390,7 @@ __global__ void __launch_bounds__(512, 4) k_expert_gemm(GemmArgs a, int nblk) {
 #pragma unroll
     for (int j = 0; j < JN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const uint32_t vmask = 0x000F000Fu;
+  const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u;
   // one chunk from stage st: 2 MFMA steps of 32 k.  Lane (ln, lq) takes the
   // codes k = 16 lq + 0..15 of its columns, step t their codes 8 t .. 8 t + 7;
   // the activation side reads the same k (segment 2 lq + t).
@@ -405,7 +412,7 @@ __global__ void __launch_bounds__(512, 4) k_expert_gemm(GemmArgs a, int nblk) {
     for (int t = 0; t < 2; ++t) {
       f16x8_t bf[JN];
 #pragma unroll
-      for (int j = 0; j < JN; ++j) bf[j] = dequant8_fast(t ? q[j].y : q[j].x, vmask, sc[j], bi[j]);
+      for (int j = 0; j < JN; ++j) bf[j] = dequant8_fast(t ? q[j].y : q[j].x, m0, m1, sc[j], bi[j]);
       const uint8_t* as = st + kStA + abase + 16 * ((2 * lq + t) ^ aswz);
 #pragma unroll
       for (int i = 0; i < IM; ++i) {
