@@ -108,10 +108,16 @@ DECODE_ERR_OFFSET = 512  # MOE_DECODE_ERR_OFFSET
 
 
 def load(path: str = LIB_PATH):
-    """Load libmoe.so; raises if it is not built."""
+    """Load libmoe.so.  When the in-tree library has not been built yet it is
+    built first (hipcc, gfx950); a build or load failure raises: there is no
+    other implementation to fall back to."""
     global _lib
     if _lib is not None:
         return _lib
+    if not os.path.exists(path) and path == LIB_PATH:
+        from . import build as _build
+        print(f"{path} is not built: building it now", flush=True)
+        _build.build()
     if not os.path.exists(path):
         raise FileNotFoundError(
             f"{path} is not built; run `python -m int4_expert_ffn_int8_amd.build`")
