@@ -204,6 +204,37 @@ def test_prefill_3300_tokens_repeatable_bits():
         np.testing.assert_array_equal(runs[1][k].view(np.uint8), runs[0][k].view(np.uint8), err_msg=k)
 
 
+def test_prefill_graph_replays_match_eager():
+    # the whole prefill block captured in a HIP graph: nothing on the path is
+    # cleared with a memset node (the grouping histogram is zeroed by the
+    # router kernel), so every replay, with eager calls in between, gives the
+    # eager bits
+    from int4_expert_ffn_int8_amd.layer import dev
+    w = synth.workload(4)  # 35B-shaped layer with the Zipf(1.1) router bias
+    L, router, experts, shared = _layer(w, seed=5)
+    T = 700  # MFMA router GEMM, several histogram chunks
+    x = dev(synth.tokens(w, 9, T=T, seed=5))
+    bias = dev(synth.zipf_bias(w))
+    b = L.buffers(T, prefill=True)
+    L.forward(x, b, bias=bias)
+    torch.cuda.synchronize()
+    eager = {k: b[k].clone() for k in ("idx", "perm", "y", "out")}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.forward(x, b, bias=bias)
+    for rep in range(3):
+        for k in eager:
+            b[k].zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in eager:
+            assert torch.equal(b[k], eager[k]), (rep, k)
+        L.forward(x, b, bias=bias)  # eager work between replays
+        torch.cuda.synchronize()
+        for k in eager:
+            assert torch.equal(b[k], eager[k]), ("eager", rep, k)
+
+
 def test_prefill_8b_shape_3300_tokens_zipf():
     # the second prefill workload: 8B-shaped layer (128 experts, top-8, no
     # shared expert), 3300 tokens, Zipf(1.1) rank bias; group sizes differ
