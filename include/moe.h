@@ -175,7 +175,9 @@ MOE_API moe_status_t moe_route(const moe_dims_t* d, const int8_t* gate_q, const 
  * LoRA delta, plus the shared expert.  [P1] Recover-LoRA paragraph, [P3]
  * "三件套" bullets: frozen int4 base plus an unmerged LoRA added on the fly.
  *   a_p = deq(Q_p) v + lora_scale * B_p (A_p v) for p in gate, up, down;
- *   h = silu(a_gate(x)) * a_up(x);  y = a_down(h)   (h is rounded to bf16).
+ *   h = silu(a_gate(x)) * a_up(x);  y = a_down(h).  h enters the down
+ *   projection as fp16 scaled by a power of two (one exponent per row on the
+ *   prefill path, per 32-column slice on the decode path), not as bf16.
  *   routed       where the routed experts live (see moe_experts_t).
  *   shared_blob  device blob of the shared expert (n_shared == 1) or NULL.
  *   x            device bf16 [T, H];  topk_idx device int32 [T, K] (the decode
