@@ -190,4 +190,11 @@ __device__ __forceinline__ void wall_wait(uint32_t ticks) {
   while (uint64_t(wall_clock64()) - t0 < ticks) __builtin_amdgcn_s_sleep(8);
 }
 
+// Row exponent: the largest magnitude m of a row is scaled into [2^14, 2^15)
+// (e may be negative); rows of zeros keep e = 0.
+__device__ __forceinline__ int row_exp(float m) {
+  if (!(m > 0.f)) return 0;
+  return max(min(ilogbf(m) - 14, 126), -100);
+}
+
 }  // namespace moe

@@ -13,7 +13,8 @@
 //     [2^14, 2^15); the epilogue multiplies the row by 2^e.  Rows of x are
 //     converted once per token (k_x16_setup, whose last workgroup also does
 //     the per-group setup), rows of the SwiGLU output h once per row after
-//     the gate/up GEMM (k_h16, from an fp32 h and its row maximum);
+//     the gate/up GEMM, from an fp32 h and its row maximum (by the LoRA-A
+//     GEMM of down, which reads every row of h anyway; by k_h16 without LoRA);
 //   * the unmerged LoRA delta ([P1] Recover-LoRA paragraph) is one extra
 //     64-wide K chunk on bf16 MFMA: the activation side holds
 //     lambda * (A v) * 2^-e as a bf16 hi + lo pair, the weight side holds B
@@ -36,12 +37,6 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// Row exponent: the largest magnitude m of a row is scaled into [2^14, 2^15)
-// (e may be negative); rows of zeros keep e = 0.
-__device__ __forceinline__ int row_exp(float m) {
-  if (!(m > 0.f)) return 0;
-  return max(min(ilogbf(m) - 14, 126), -100);
-}
 
 // ---------------------------------------------------------------------------
 // Expert-GEMM setup for the 256 threads of one workgroup: group row starts,

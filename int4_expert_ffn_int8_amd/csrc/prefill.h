@@ -36,6 +36,8 @@ struct GemmArgs {
   uint32_t* hmax;             // [NR] float bits of max |h| per row (zeroed by the setup)
   const uint16_t* hs;         // [NR][I] fp16 h * 2^-eh[s]
   const int32_t* eh;          // [NR]
+  uint16_t* hs_out;           // where the LoRA-A GEMM of down writes hs (and eh_out eh)
+  int32_t* eh_out;
   const uint16_t* u;          // [NR][64] lambda * (A_g x, A_u x) * 2^-ex as bf16 hi/lo pairs
   uint16_t* u_out;
   const uint16_t* ud;         // [NR][64] lambda * (A_d h) * 2^-eh as bf16 hi/lo pairs

@@ -10,6 +10,8 @@
 // scale per 64-column chunk) and the two skinny LoRA-A GEMMs of the unmerged
 // delta ([P1] Recover-LoRA paragraph), whose outputs lambda * (A v) are
 // stored as bf16 hi + lo pairs in the row-scaled domain of the expert GEMMs.
+// The LoRA-A GEMM of down also converts h (fp32, from the gate/up epilogue)
+// into the fp16 rows with row exponents that the down GEMM reads.
 //
 // Row space of the expert GEMMs ("sorted rows"): s in [0, T*K) are the routed
 // pairs in perm order (expert by expert, ascending pair id), s in [T*K,
@@ -219,6 +221,21 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
     else if (MODE == kLoraGU) arow[i] = a.x + size_t(token_of(a, s)) * a.H;
     else arow[i] = a.hs + size_t(s) * a.I;
   }
+  // LoRA-A of down reads h in fp32 and converts each row to fp16(h * 2^-e)
+  // itself (e from the row maximum of the gate/up epilogue), writing the
+  // converted rows and exponents for the down GEMM as it goes: every row of
+  // the sorted row space is read by exactly one workgroup, once.
+  constexpr bool kH16 = (MODE == kLoraD);
+  const float* hrow[C::A_SEGS];
+  int hexp[C::A_SEGS], hrs[C::A_SEGS];
+#pragma unroll
+  for (int i = 0; i < C::A_SEGS; ++i) {
+    const int s = row0 + ((tid + 256 * i) >> 3);
+    const bool ok = kH16 && s < row_end;
+    hrs[i] = ok ? s : -1;
+    hrow[i] = ok ? a.hf + size_t(s) * a.I : nullptr;
+    hexp[i] = ok ? row_exp(__uint_as_float(a.hmax[s])) : 0;
+  }
 
   const int nchunks = Kdim / BK;
 
@@ -230,6 +247,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
 
   // register staging of one chunk
   uint4 ra[C::A_SEGS];
+  float4 rh[kH16 ? 2 * C::A_SEGS : 1];  // fp32 h segments (LoRA-A of down)
   // B staging: int4 -> 16B codes + scale/bias; int8 -> 16B codes; bf16 -> 16B
   constexpr int B_SEGS_INT8 = (BN * 4 + 255) / 256;   // 16B = 16 codes
   constexpr int B_SEGS_BF16 = (BN * 8 + 255) / 256;   // 16B = 8 bf16
@@ -238,10 +256,20 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
 
   auto load_chunk = [&](int c) {
     const int k0 = c * BK;
+    if constexpr (kH16) {
 #pragma unroll
-    for (int i = 0; i < C::A_SEGS; ++i) {
-      const uint16_t* src = arow[i];
-      ra[i] = src ? *reinterpret_cast<const uint4*>(src + k0 + 8 * aseg[i]) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < C::A_SEGS; ++i) {
+        const float* src = hrow[i];
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        rh[2 * i] = src ? *reinterpret_cast<const float4*>(src + k0 + 8 * aseg[i]) : z;
+        rh[2 * i + 1] = src ? *reinterpret_cast<const float4*>(src + k0 + 8 * aseg[i] + 4) : z;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::A_SEGS; ++i) {
+        const uint16_t* src = arow[i];
+        ra[i] = src ? *reinterpret_cast<const uint4*>(src + k0 + 8 * aseg[i]) : make_uint4(0, 0, 0, 0);
+      }
     }
     if (MODE == kRouter) {
 #pragma unroll
@@ -295,6 +323,23 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   constexpr bool kPost = (MODE == kRouter);
 
   auto store_chunk = [&](int c) {
+    if constexpr (kH16) {  // fp16(h * 2^-e), as the down GEMM reads it
+#pragma unroll
+      for (int i = 0; i < C::A_SEGS; ++i) {
+        const int e = hexp[i];
+        const float4 v0 = rh[2 * i], v1 = rh[2 * i + 1];
+        const f16x2_t p0 = {_Float16(ldexpf(v0.x, -e)), _Float16(ldexpf(v0.y, -e))};
+        const f16x2_t p1 = {_Float16(ldexpf(v0.z, -e)), _Float16(ldexpf(v0.w, -e))};
+        const f16x2_t p2 = {_Float16(ldexpf(v1.x, -e)), _Float16(ldexpf(v1.y, -e))};
+        const f16x2_t p3 = {_Float16(ldexpf(v1.z, -e)), _Float16(ldexpf(v1.w, -e))};
+        ra[i] = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+        if (hrs[i] >= 0) {
+          *reinterpret_cast<uint4*>(a.hs_out + size_t(hrs[i]) * a.I + c * BK + 8 * aseg[i]) = ra[i];
+          if (c == 0 && aseg[i] == 0) a.eh_out[hrs[i]] = e;
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < C::A_SEGS; ++i) {
       const int sidx = tid + 256 * i;
@@ -511,10 +556,15 @@ hipError_t launch_prefill_experts(const GemmArgs& a, const int32_t* counts, Expe
   }
   e = launch_expert_gemm(kGemmGateUp, a, mt, st);
   if (e != hipSuccess) return e;
-  e = launch_h16(a.hf, a.hmax, a.gstart + a.E + 1, NR, a.I, hs16, eh, st);
-  if (e != hipSuccess) return e;
-  if (a.r > 0)
-    hipLaunchKernelGGL((k_gemm<kLoraD, kLoraBM, 64, 2, 2>), dim3(mt * (kPrefillBM / kLoraBM)), dim3(256), 0, st, a);
+  if (a.r > 0) {  // LoRA-A of down, which also writes h as fp16 rows with their exponents
+    GemmArgs ad = a;
+    ad.hs_out = hs16;
+    ad.eh_out = eh;
+    hipLaunchKernelGGL((k_gemm<kLoraD, kLoraBM, 64, 2, 2>), dim3(mt * (kPrefillBM / kLoraBM)), dim3(256), 0, st, ad);
+  } else {
+    e = launch_h16(a.hf, a.hmax, a.gstart + a.E + 1, NR, a.I, hs16, eh, st);
+    if (e != hipSuccess) return e;
+  }
   return launch_expert_gemm(kGemmDown, a, mt, st);
 }
 
