@@ -145,6 +145,39 @@ def test_router_hand_example_ties():
     assert list(O.topk_weights(l, O.select_topk(l, 1))) == g["K1_w"]
 
 
+def test_router_bias_moves_selection_and_weights():
+    # the skewed prefill's per-expert bias enters before both the selection
+    # and the softmax: dropping it, or adding it to only one of the two,
+    # changes the experts or their weights
+    g = GOLD["router_bias"]
+    rq, rs = _router_from_codes(g["codes"], g["scale"], g["H"])
+    x = np.full((1, g["H"]), f2bits(g["x"]), np.uint16)
+    bias = np.array(g["bias"], np.float32)
+    l = O.router_logits(rq, rs, x, bias)[0]
+    assert list(l) == g["logits"]
+    sel = O.select_topk(l, 2)
+    assert list(sel) == g["K2_idx"]
+    assert np.allclose(O.topk_weights(l, sel), g["K2_w"], rtol=1e-15, atol=0)
+    assert np.allclose(O.topk_weights(l, sel, norm_topk=False), g["K2_w_full_softmax"],
+                       rtol=1e-15, atol=0)
+    # the same through the whole block: two constant experts with different
+    # outputs, so the weights show in the block output
+    H = g["H"]
+    experts = [const_expert(H, 64, 1, 1, 0.015625, 0.0),       # y = sigmoid(1)
+               const_expert(H, 64, 1, 1, 0.015625, 0.0,
+                            A={"gate": 0.015625}, B={"gate": 1.0}),  # y = 2 sigmoid(2)
+               const_expert(H, 64, 1, 0, 0.0, 0.0),
+               const_expert(H, 64, 1, 0, 0.0, 0.0)]
+    router = {"router_q": rq, "router_s": rs}
+    w = dict(H=H, E=4, K=2, lora_scale=1.0)
+    o, parts = O.moe_block(w, router, lambda e: experts[e], x, bias=bias, return_parts=True)
+    assert parts["idx"].tolist() == [g["K2_idx"]]
+    y0 = GOLD["expert_base_only"]["y"]
+    y1 = GOLD["expert_lora_gate"]["y"]
+    want = g["K2_w"][0] * y0 + g["K2_w"][1] * y1
+    assert np.allclose(o, want, rtol=1e-15, atol=0)
+
+
 def test_router_zero_input():
     w = synth.workload(0)
     r = synth.router_tensors(w, 0)
@@ -406,6 +439,25 @@ def test_stack_layer_with_zero_block_is_identity():
     h = synth.tokens(w, 5, T=2)
     out = O.stack_layer(w, router, lambda e: zero, h)
     assert np.array_equal(out, h)
+
+
+def test_stack_layer_hand_example_norm_and_rounding():
+    # h' = bf16(h + MoE(bf16(RMSNorm(h)))): a two-valued h whose RMSNorm
+    # rounds visibly to bf16, through a constant expert; the block input, the
+    # unrounded block output and the layer output all have closed forms
+    g = GOLD["stack_layer_norm"]
+    H, I = g["H"], g["I"]
+    ex = const_expert(H, I, 1, 1, 0.015625, 0.0)
+    rq, rs = _router_from_codes([1] * g["E"], 0.015625, H)
+    w = dict(H=H, E=g["E"], K=g["K"], lora_scale=1.0)
+    h = np.array([[f2bits(g["h_hi"])] * (H // 2) + [f2bits(g["h_lo"])] * (H // 2)], np.uint16)
+    out, parts = O.stack_layer(w, {"router_q": rq, "router_s": rs}, lambda e: ex, h,
+                               eps=g["eps"], return_parts=True)
+    xn = [bfv(v) for v in parts["xn_bits"][0]]
+    assert xn == [g["xn_hi"]] * (H // 2) + [g["xn_lo"]] * (H // 2)
+    assert parts["idx"].tolist() == [[0]]
+    assert np.allclose(parts["o"], g["o"], rtol=1e-14, atol=0)
+    assert [bfv(v) for v in out[0]] == [g["out_hi"]] * (H // 2) + [g["out_lo"]] * (H // 2)
 
 
 def test_prerouter_zero_head_and_brute_force():
