@@ -121,8 +121,10 @@ MOE_API moe_status_t moe_pack_expert(int32_t H, int32_t I, int32_t r,
  *   read_delay_ns   modeled storage latency of the host copy ([P2] Prerouter
  *                   and SSD paragraphs: the benefit of early loads grows with
  *                   storage latency): in moe_block_decode(_exec), a
- *                   workgroup that reads a non-resident expert first waits
- *                   this long (a bounded wall-clock wait).  0: none; at most
+ *                   workgroup that reads non-resident experts first waits
+ *                   this long, once however many of its experts missed (a
+ *                   bounded wall-clock wait; its reads are issued together).
+ *                   0: none; at most
  *                   MOE_MAX_READ_DELAY_NS (else MOE_EINVAL).  The other
  *                   calls ignore it. */
 #define MOE_MAX_READ_DELAY_NS 1000000u

@@ -116,8 +116,10 @@ __device__ __forceinline__ int pair_of_unit(const FusedArgs& a, int q) {
   return (q / a.K) * KS + q % a.K;
 }
 
-// blob of routed expert e (pool lookup)
-__device__ __forceinline__ const uint8_t* expert_blob(const FusedArgs& a, int e, bool count) {
+// blob of routed expert e (pool lookup); `miss` is set when the blob is the
+// pinned host copy (the expert is not resident in a slot)
+__device__ __forceinline__ const uint8_t* expert_blob_at(const FusedArgs& a, int e, bool count,
+                                                         bool& miss) {
   if (a.src.expert_to_slot == nullptr) return a.src.slots + size_t(e) * a.src.stride;
   const int s = a.src.expert_to_slot[e];
   if (count && a.src.counters) {
@@ -125,8 +127,22 @@ __device__ __forceinline__ const uint8_t* expert_blob(const FusedArgs& a, int e,
     if (s >= 0) atomicAdd(&a.src.counters[0], 1ull);
   }
   if (s >= 0) return a.src.slots + size_t(s) * a.src.stride;
-  if (a.src.delay_ticks) wall_wait(a.src.delay_ticks);  // modeled storage latency
+  miss = true;
   return a.src.host_blobs + size_t(e) * a.src.stride;
+}
+
+// The modeled storage latency of the host reads a workgroup is about to
+// issue: one wait however many of its blobs missed (the reads are issued
+// together, so they wait in parallel).
+__device__ __forceinline__ void storage_latency(const FusedArgs& a, bool miss) {
+  if (miss && a.src.delay_ticks) wall_wait(a.src.delay_ticks);
+}
+
+__device__ __forceinline__ const uint8_t* expert_blob(const FusedArgs& a, int e, bool count) {
+  bool miss = false;
+  const uint8_t* b = expert_blob_at(a, e, count, miss);
+  storage_latency(a, miss);
+  return b;
 }
 
 // Expert id of routed pair p, published by the top-K (workgroup-uniform).
@@ -518,12 +534,25 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
     lds_idx[tid] = (k < a.K) ? int(uint32_t(poll_word(a, &a.route[t * a.K + k], tag))) : -1;
   }
   __syncthreads();
+  // resident blobs are fetched at once; if any blob is the host copy, one
+  // modeled latency precedes all of this thread's host reads
+  uint32_t missed = 0;
 #pragma unroll
   for (int p = 0; p < kFusedMaxP; ++p) {
     if (p < P && (p % KS) < a.K) {
-      bl[p] = expert_blob(a, lds_idx[p], d == 0 && tid == 0);  // one count per lookup
-      fetch(p);
+      bool m = false;
+      bl[p] = expert_blob_at(a, lds_idx[p], d == 0 && tid == 0, m);  // one count per lookup
+      if (m)
+        missed |= 1u << p;
+      else
+        fetch(p);
     }
+  }
+  if (missed) {
+    storage_latency(a, true);
+#pragma unroll
+    for (int p = 0; p < kFusedMaxP; ++p)
+      if ((missed >> p) & 1u) fetch(p);
   }
   // wait for the last h word, then load every pair's h, v partials and
   // routing weights until all carry this launch's tag

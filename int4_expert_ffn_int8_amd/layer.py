@@ -302,6 +302,12 @@ class MoeStack:
         pred = self.pred_host.numpy() if self.prerouter is not None else None
         return self.pool.update(self.idx_host.numpy(), pred, self.max_fills, self.side)
 
+    def error_word(self) -> int:
+        """Sticky timeout flag shared by every layer's fused launch (0 = every
+        wait of every step completed).  Reading it synchronises."""
+        o = B.DECODE_ERR_OFFSET
+        return int(self.ws[o:o + 4].view(torch.int32).item())
+
     def hit_counts(self):
         """(lookups served from a slot, all lookups) summed over layers."""
         c = self.counters.sum(0).tolist()

@@ -7,9 +7,12 @@ Recipe (the pages print no weights, so every value is drawn here):
   independent codes, low nibble first), per-64-column-group scale
   |N(0, 0.02)| and bias N(0, 0.01), both rounded to bf16;
 * LoRA factors A [r, in] and B [out, r]: N(0, 0.02) rounded to bf16;
-* router gate and shared-expert gate: int8 codes uniform in [-127, 127] with a
-  per-64-column-group fp32 scale |N(0, 0.02)| / 127 (codes and scales are
-  drawn directly, the way the expert codes are, so no quantiser is needed);
+* router gate and shared-expert gate: fp32 weights N(0, 0.02), stored as
+  symmetric int8 codes with one fp32 scale per 64 columns, the group's largest
+  magnitude / 127 (codes = weights / scale rounded to nearest, ties to even).
+  At H = 2048 and x ~ N(0, 1) this gives router logits of standard deviation
+  about 0.02 * sqrt(2048) = 0.9.  This is how the inputs are made; the method
+  itself only ever reads the stored codes and scales;
 * token activations x: N(0, 1) rounded to bf16;
 * Zipf rank bias for the skewed prefill: a seeded permutation of ranks 1..E,
   bias[e] = -s * ln(rank[e]);
@@ -122,23 +125,24 @@ def expert_tensors(w: dict, layer: int, expert: int, seed: int = 0) -> dict:
     return out
 
 
+def _int8_gate_codes(rng, rows: int, H: int):
+    """Draw fp32 N(0, 0.02) gate weights [rows, H] and store them as int8
+    codes with a per-64-column fp32 scale (group max magnitude / 127)."""
+    v = rng.standard_normal(size=(rows, H), dtype=np.float32) * np.float32(0.02)
+    g = v.reshape(rows, H // 64, 64).astype(np.float64)
+    s = (np.abs(g).max(axis=2) / 127.0).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1)).astype(np.float64)
+    q = np.clip(np.rint(g / safe[..., None]), -127, 127).astype(np.int8)
+    return q.reshape(rows, H), s
+
+
 def router_tensors(w: dict, layer: int, seed: int = 0) -> dict:
     """int8 router gate [E, H] + fp32 scales [E, H/64]; shared gate [1, H]."""
     H, E, wid = w["H"], w["E"], w["id"]
-    G = H // 64
-    out = {
-        "router_q": _rng(seed, wid, layer, "router_q").integers(
-            -127, 128, size=(E, H), dtype=np.int8),
-        "router_s": (np.abs(_rng(seed, wid, layer, "router_s").standard_normal(
-            size=(E, G), dtype=np.float32)) * np.float32(0.02 / 127)
-        ).astype(np.float32),
-    }
+    out = {}
+    out["router_q"], out["router_s"] = _int8_gate_codes(_rng(seed, wid, layer, "router_q"), E, H)
     if w.get("n_shared", 0):
-        out["sgate_q"] = _rng(seed, wid, layer, "sgate_q").integers(
-            -127, 128, size=(1, H), dtype=np.int8)
-        out["sgate_s"] = (np.abs(_rng(seed, wid, layer, "sgate_s").standard_normal(
-            size=(1, G), dtype=np.float32)) * np.float32(0.02 / 127)
-        ).astype(np.float32)
+        out["sgate_q"], out["sgate_s"] = _int8_gate_codes(_rng(seed, wid, layer, "sgate_q"), 1, H)
     return out
 
 

@@ -173,6 +173,8 @@ def test_predict_mode_stack_pool_resident_and_oracle():
     np.testing.assert_array_equal(c[1:, 0], c[1:, 1])
     for st in (pooled, delayed):
         st.pool.sync(st.side)
+    for st in (resident, pooled, delayed):
+        assert st.error_word() == 0
 
 
 def test_predict_mode_with_feature_heads():
@@ -220,3 +222,4 @@ def test_predict_mode_with_feature_heads():
         prev_pred = pred.copy()
     assert checked >= (nl - 1) * steps // 2
     pooled.pool.sync(pooled.side)
+    assert resident.error_word() == 0 and pooled.error_word() == 0

@@ -255,7 +255,8 @@ def test_prefill_through_pool_cold_and_warm_match_resident():
     # prefill with the routed experts behind an HBM slot pool over a pinned
     # host master copy: cold (no expert resident: the GEMMs read the host
     # copy) and warm (the touched experts filled into slots) give the same
-    # bits as the all-resident layer, and the lookups are counted
+    # bits as the all-resident layer, match the oracle, and the lookups are
+    # counted
     from int4_expert_ffn_int8_amd import binding as B
     from int4_expert_ffn_int8_amd.layer import dev, pack_experts
     w = synth.workload(0)
@@ -267,6 +268,8 @@ def test_prefill_through_pool_cold_and_warm_match_resident():
     torch.cuda.synchronize()
     y_res = b0["y"].cpu().numpy().copy()
     out_res = b0["out"].cpu().numpy().copy()
+    o_ref, parts = O.moe_block(w, router, lambda e: experts[e], xb, shared=shared,
+                               return_parts=True)
     counts = b0["counts"].cpu().numpy()
     touched = np.nonzero(counts)[0].astype(np.int32)
 
@@ -289,6 +292,15 @@ def test_prefill_through_pool_cold_and_warm_match_resident():
             torch.cuda.synchronize()
             np.testing.assert_array_equal(b["y"].cpu().numpy(), y_res, err_msg=phase)
             np.testing.assert_array_equal(b["out"].cpu().numpy(), out_res, err_msg=phase)
+            # and against the oracle on the same inputs
+            gi = b["idx"].cpu().numpy()
+            near = check_routing(b["logits"].cpu().numpy(), gi, b["w"].cpu().numpy(),
+                                 parts["logits"], w["K"], True, max_near_ties=2)
+            assert_close_rms(b["y"].cpu().numpy(), _oracle_y(w, experts, shared, xb, gi),
+                             f"pooled prefill y ({phase})")
+            ok = [t for t in range(300) if t not in near]
+            assert_bf16_output_close(b["out"].cpu().numpy().view(np.uint16)[ok], o_ref[ok],
+                                     f"pooled prefill output ({phase})")
             hits, lookups = (int(v) for v in counters.cpu().numpy())
             assert lookups == len(touched)
             assert hits == (0 if phase == "cold" else min(len(touched), 8))

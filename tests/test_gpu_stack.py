@@ -62,6 +62,7 @@ def test_stack24_shapes_teacher_forced_per_layer():
             assert_bf16_output_close(got, O.bf16_to_f64(h_in) + parts["o"],
                                      f"stack24 step {step} layer {l}")
             h_in = got  # teacher forcing: the oracle's next input is the GPU's output
+    assert st.error_word() == 0
 
 
 def _pool_stack(w, routers, shared_dev, blobs, heads, pred_k, **kw):
@@ -111,3 +112,5 @@ def test_pool_results_do_not_depend_on_residency():
     # the device table mirrors the planner's table
     for l in range(nl):
         np.testing.assert_array_equal(pooled.table[l].cpu().numpy(), pooled.pool.table(l))
+    for st in (resident, pooled, never):
+        assert st.error_word() == 0
