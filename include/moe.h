@@ -277,6 +277,31 @@ MOE_API moe_status_t moe_block_decode_exec(const moe_dims_t* d, const int8_t* ga
                                            float* topk_w, uint16_t* out, void* ws,
                                            size_t ws_bytes, void* stream);
 
+/* moe_block_decode_noalloc: moe_block_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The same kernel and the same results as
+ * moe_block_decode; the workspace is a library-owned device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU instead of a caller buffer, and this call
+ * never allocates or frees memory.
+ *   Arguments, limits and outputs are moe_block_decode's (no ws, ws_bytes).
+ *   error_out  device int32 or NULL: receives this call's timeout flag (1 if
+ *              a wait exceeded its bound, else 0); the flag is then cleared.
+ *   Scratch: the first call on a device looks up that device's array and
+ *   zeroes it with a kernel on `stream`; each later call finds the array as
+ *   the previous call on that device left it (its control words consistent).
+ *   Shapes whose workspace layout exceeds MOE_NOALLOC_SCRATCH_BYTES return
+ *   MOE_EUNSUPPORTED before any device work.  Every call on one GPU shares
+ *   that GPU's array: calls that overlap in time on one GPU (different
+ *   streams or threads without ordering) race and give undefined results. */
+#define MOE_NOALLOC_SCRATCH_BYTES 524288
+MOE_API moe_status_t moe_block_decode_noalloc(const moe_dims_t* d, const int8_t* gate_q,
+                                              const float* gate_s, const int8_t* sgate_q,
+                                              const float* sgate_s, const moe_experts_t* routed,
+                                              const void* shared_blob, const uint16_t* h_in,
+                                              int32_t T, int32_t flags, float eps,
+                                              int32_t* topk_idx, float* topk_w, uint16_t* out,
+                                              int32_t* error_out, void* stream);
+
 /* ---------------------------------------------------------------------------
  * prerouter_predict: the Prerouter head.  [P1] Prerouter paragraph and [P2]
  * double-shift paragraph: a light MLP after layer N predicts layer N+1's

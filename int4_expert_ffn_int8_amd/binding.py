@@ -64,6 +64,9 @@ _SIGS = {
     "moe_block_decode_exec": (c_i32, [ctypes.POINTER(MoeDims), c_vp, c_vp, c_vp, c_vp,
                                       ctypes.POINTER(MoeExperts), c_vp, c_vp, c_i32, c_i32, c_f32,
                                       c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "moe_block_decode_noalloc": (c_i32, [ctypes.POINTER(MoeDims), c_vp, c_vp, c_vp, c_vp,
+                                         ctypes.POINTER(MoeExperts), c_vp, c_vp, c_i32, c_i32,
+                                         c_f32, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "prerouter_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32]),
     "moe_lru_create": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_vp)]),
     "moe_lru_destroy": (None, [c_vp]),
@@ -94,7 +97,7 @@ HEADER_SYMBOLS = [
     "moe_last_error", "moe_expert_blob_bytes", "moe_pack_expert", "moe_workspace_bytes",
     "moe_route", "moe_expert_forward", "moe_combine", "moe_rmsnorm",
     "moe_block_decode_workspace_bytes", "moe_workspace_init", "moe_block_decode",
-    "moe_block_decode_exec",
+    "moe_block_decode_exec", "moe_block_decode_noalloc",
     "prerouter_workspace_bytes", "prerouter_predict", "prerouter_predict_feat",
     "moe_lru_create", "moe_lru_destroy", "moe_lru_plan", "moe_lru_table", "moe_lru_stats",
     "moe_pool_create", "moe_pool_destroy", "moe_pool_layer", "moe_pool_update",
@@ -264,6 +267,16 @@ def moe_block_decode_exec(d, gate_q, gate_s, sgate_q, sgate_s, routed: MoeExpert
                                         ptr(topk_w), ptr(out), ptr(ws),
                                         ws.numel() * ws.element_size() if ws is not None else 0,
                                         stream_ptr(stream)))
+
+
+def moe_block_decode_noalloc(d, gate_q, gate_s, sgate_q, sgate_s, routed: MoeExperts,
+                             shared_blob, h_in, T, flags, eps, topk_idx, topk_w, out,
+                             error_out=None, stream=None) -> None:
+    _check(load().moe_block_decode_noalloc(ctypes.byref(d), ptr(gate_q), ptr(gate_s),
+                                           ptr(sgate_q), ptr(sgate_s), ctypes.byref(routed),
+                                           ptr(shared_blob), ptr(h_in), T, flags, eps,
+                                           ptr(topk_idx), ptr(topk_w), ptr(out), ptr(error_out),
+                                           stream_ptr(stream)))
 
 
 # ---- expert pool ------------------------------------------------------------

@@ -268,14 +268,13 @@ uint32_t wall_ticks(uint32_t ns) {
 
 }  // namespace moe
 
-namespace {
+namespace moe {
 
-moe_status_t block_decode(const char* fn, const moe_dims_t* d, const int8_t* gate_q,
-                          const float* gate_s, const int8_t* sgate_q, const float* sgate_s,
-                          const moe_experts_t* routed, const void* shared_blob,
-                          const uint16_t* h_in, int32_t T, int32_t flags, float eps,
-                          const int32_t* exec_idx, int32_t* topk_idx, float* topk_w,
-                          uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+moe_status_t block_decode_check(const char* fn, const moe_dims_t* d, const int8_t* gate_q,
+                                const float* gate_s, const int8_t* sgate_q, const float* sgate_s,
+                                const moe_experts_t* routed, const void* shared_blob,
+                                const uint16_t* h_in, int32_t T, int32_t flags, float eps,
+                                uint16_t* out) {
   moe_status_t st = check_dims(d, fn);
   if (st != MOE_OK) return st;
   if (T < 0) return fail(MOE_EINVAL, "%s: T=%d is negative", fn, T);
@@ -303,6 +302,16 @@ moe_status_t block_decode(const char* fn, const moe_dims_t* d, const int8_t* gat
                 MOE_MAX_READ_DELAY_NS);
   if (T == 0) return MOE_OK;
   if (!gate_q || !gate_s || !h_in || !out) return fail(MOE_EINVAL, "%s: null pointer", fn);
+  return MOE_OK;
+}
+
+moe_status_t block_decode_launch(const char* fn, const moe_dims_t* d, const int8_t* gate_q,
+                                 const float* gate_s, const int8_t* sgate_q, const float* sgate_s,
+                                 const moe_experts_t* routed, const void* shared_blob,
+                                 const uint16_t* h_in, int32_t T, int32_t flags, float eps,
+                                 const int32_t* exec_idx, int32_t* topk_idx, float* topk_w,
+                                 uint16_t* out, void* ws, size_t ws_bytes, int32_t* err_out,
+                                 void* stream) {
   const FusedWs W = fused_ws_layout(T, d->E, d->K, d->n_shared, d->I, d->r);
   if (!ws || ws_bytes < W.total)
     return fail(MOE_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, W.total);
@@ -337,6 +346,7 @@ moe_status_t block_decode(const char* fn, const moe_dims_t* d, const int8_t* gat
   a.user_idx = topk_idx;
   a.user_w = topk_w;
   a.exec_idx = exec_idx;
+  a.err_out = err_out;
   a.sync = reinterpret_cast<int*>(wsb + W.sync);
   a.logits = reinterpret_cast<tword_t*>(wsb + W.logits);
   a.route = reinterpret_cast<tword_t*>(wsb + W.route);
@@ -346,6 +356,24 @@ moe_status_t block_decode(const char* fn, const moe_dims_t* d, const int8_t* gat
   a.hexp = reinterpret_cast<tword_t*>(wsb + W.hexp);
   a.vpart = reinterpret_cast<tword_t*>(wsb + W.vpart);
   return hip_status(launch_fused(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace moe
+
+namespace {
+
+moe_status_t block_decode(const char* fn, const moe_dims_t* d, const int8_t* gate_q,
+                          const float* gate_s, const int8_t* sgate_q, const float* sgate_s,
+                          const moe_experts_t* routed, const void* shared_blob,
+                          const uint16_t* h_in, int32_t T, int32_t flags, float eps,
+                          const int32_t* exec_idx, int32_t* topk_idx, float* topk_w,
+                          uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = block_decode_check(fn, d, gate_q, gate_s, sgate_q, sgate_s, routed,
+                                       shared_blob, h_in, T, flags, eps, out);
+  if (st != MOE_OK || T == 0) return st;
+  return block_decode_launch(fn, d, gate_q, gate_s, sgate_q, sgate_s, routed, shared_blob, h_in, T,
+                             flags, eps, exec_idx, topk_idx, topk_w, out, ws, ws_bytes, nullptr,
+                             stream);
 }
 
 }  // namespace

@@ -46,6 +46,8 @@ struct FusedArgs {
   int32_t* user_idx;     // [T][K] or null
   float* user_w;         // [T][K] or null
   const int32_t* exec_idx;  // [T][K] experts to execute (prediction-as-routing) or null
+  int32_t* err_out;         // device int32 or null: the last workgroup moves the sticky
+                            // error word here and clears it
   // workspace
   int* sync;
   tword_t* logits;  // [T][E + 1]   router logits; column E: shared-gate logit
@@ -82,5 +84,20 @@ inline FusedWs fused_ws_layout(int T, int E, int K, int S, int I, int r) {
 bool fused_shape_supported(int H, int I, int r);
 hipError_t launch_fused(const FusedArgs& a, hipStream_t st);
 hipError_t launch_zero_ints(int* p, int n, hipStream_t st);
+
+// Argument checks of moe_block_decode(_exec) (no device work), and the launch
+// on a caller-chosen workspace base (ws_bytes is checked against the layout).
+moe_status_t block_decode_check(const char* fn, const moe_dims_t* d, const int8_t* gate_q,
+                                const float* gate_s, const int8_t* sgate_q, const float* sgate_s,
+                                const moe_experts_t* routed, const void* shared_blob,
+                                const uint16_t* h_in, int32_t T, int32_t flags, float eps,
+                                uint16_t* out);
+moe_status_t block_decode_launch(const char* fn, const moe_dims_t* d, const int8_t* gate_q,
+                                 const float* gate_s, const int8_t* sgate_q, const float* sgate_s,
+                                 const moe_experts_t* routed, const void* shared_blob,
+                                 const uint16_t* h_in, int32_t T, int32_t flags, float eps,
+                                 const int32_t* exec_idx, int32_t* topk_idx, float* topk_w,
+                                 uint16_t* out, void* ws, size_t ws_bytes, int32_t* err_out,
+                                 void* stream);
 
 }  // namespace moe

@@ -702,6 +702,10 @@ __global__ void __launch_bounds__(256) k_fused_decode(FusedArgs a) {
   __syncthreads();
   if (threadIdx.x == 0 && add_dev(slot(a, kSlotDone), 1) == a.total - 1) {
     const int e = ld_dev(slot(a, kSlotEpoch));
+    if (a.err_out) {  // every other workgroup has finished: the word is final
+      *a.err_out = ld_dev(slot(a, kSlotErr));
+      st_dev(slot(a, kSlotErr), 0);
+    }
     st_dev(slot(a, kSlotDone), 0);
     st_dev(slot(a, kSlotEpoch), e + 1);
   }

@@ -188,3 +188,21 @@ def test_pack_rejects_codes_above_15(B):
     blob = np.zeros(B.moe_expert_blob_bytes(w["H"], w["I"], w["r"]), np.uint8)
     with pytest.raises(B.MoeError):
         B.moe_pack_expert(w["H"], w["I"], w["r"], ex, blob)
+
+
+def test_block_decode_noalloc_validates_before_device_work(B):
+    # the allocation-free decode entry point checks its arguments before it
+    # looks up or touches its device scratch: no GPU is needed for these
+    lib = B.load()
+    fake = 1 << 40
+    ex = B.experts_struct(fake, 256)
+    d = B.dims(2048, 512, 256, 4, 16, 1)
+    args = lambda T, dd=d, flags=0: (B.ctypes.byref(dd), fake, fake, fake, fake,
+                                     B.ctypes.byref(ex), fake, fake, T, flags, 1e-6, None, None,
+                                     fake, None, 0)
+    assert lib.moe_block_decode_noalloc(*args(0)) == 0          # T == 0: no-op
+    assert lib.moe_block_decode_noalloc(*args(2)) == 2          # 10 pairs > 8
+    assert lib.moe_block_decode_noalloc(*args(-1)) == 1
+    assert lib.moe_block_decode_noalloc(*args(1, flags=8)) == 1
+    assert lib.moe_block_decode_noalloc(*args(1, dd=B.dims(2048, 512, 256, 4, 17, 1))) == 2
+    assert b"noalloc" in lib.moe_last_error()
