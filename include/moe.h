@@ -95,6 +95,10 @@ MOE_API size_t moe_expert_blob_bytes(int32_t H, int32_t I, int32_t r);
  *   q_p  uint8  [out, in]     codes 0..15 (values above 15 -> MOE_EINVAL)
  *   s_p  bf16   [out, in/64]  scale, b_p bf16 [out, in/64] bias:
  *        w[j, i] = s[j, i/64] * q[j, i] + b[j, i/64]
+ *        The prefill GEMMs dequantise to fp16, so every group must satisfy
+ *        |s|, |b|, |15 s + b| <= 65504 (fp16's largest finite value), all
+ *        finite; otherwise MOE_EUNSUPPORTED.  Scales below fp16's normal
+ *        range (2^-14) keep 2^-24 absolute resolution there.
  *   A_p  bf16   [r, in],  B_p bf16 [out, r]  (may be NULL when r == 0)  */
 MOE_API moe_status_t moe_pack_expert(int32_t H, int32_t I, int32_t r,
                              const uint8_t* q_gate, const uint16_t* s_gate, const uint16_t* b_gate,

@@ -14,7 +14,9 @@ import os
 import torch  # loads the HIP runtime that libmoe shares (same soname)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe.so")
+# MOE_LIB_PATH selects another build of the same library (the CPU tests use
+# it for the host-sanitized build).
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(HERE, "libmoe.so")
 
 c_i32, c_f32, c_sz, c_vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
@@ -117,7 +119,7 @@ def load(path: str = LIB_PATH):
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(path) and path == LIB_PATH:
+    if not os.path.exists(path) and path == os.path.join(HERE, "libmoe.so"):
         from . import build as _build
         print(f"{path} is not built: building it now", flush=True)
         _build.build()

@@ -30,14 +30,24 @@ COMMON = [
 ]
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer variant (CPU tests
+# only): each -fsanitize= applies to the host pass alone, device code is built
+# as usual.  The sanitizer runtime is clang's shared one, preloaded by the test.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host",
+            "-fno-omit-frame-pointer", "-g"]
+SAN_BUILD = os.path.join(HERE, "_build_san")
+SAN_LIB = os.path.join(SAN_BUILD, "libmoe_san.so")
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *extra, *lang, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
@@ -59,6 +69,37 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+def build_sanitized(jobs: int | None = None) -> str:
+    """libmoe_san.so: the same sources with host-side ASan + UBSan."""
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or min(8, len(srcs))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda f: _compile(f, SAN_BUILD, SANITIZE), srcs))
+    tmp = SAN_LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host",
+           "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libsan",
+           "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
+def sanitizer_runtime() -> str | None:
+    """Path of clang's shared ASan runtime (it also carries UBSan's handlers)."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+        return path
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib",
+                                         "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    return hits[-1] if hits else None
 
 
 if __name__ == "__main__":

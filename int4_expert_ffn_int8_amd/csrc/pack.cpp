@@ -4,6 +4,7 @@
 // release layout needed several scattered reads per expert and was repacked
 // so one expert is one sequential read.  The blob below is that idea for HBM:
 // one contiguous block per expert, which is also one expert-pool slot.
+#include <math.h>
 #include <string.h>
 
 #include "moe_internal.h"
@@ -29,11 +30,29 @@ bool pack_code_row(const uint8_t* q, int n, uint8_t* dst) {
   return true;
 }
 
-void pack_sb_row(const uint16_t* s, const uint16_t* b, int groups, uint8_t* dst) {
+float bf16_value(uint16_t v) {
+  const uint32_t u = uint32_t(v) << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+// The prefill GEMMs dequantise in fp16 (w = fp16(s q + b)), so every weight a
+// group can hold, and its scale and bias, must lie within fp16's finite range.
+constexpr float kF16Max = 65504.0f;
+bool group_fits_f16(uint16_t s, uint16_t b) {
+  const double sv = bf16_value(s), bv = bf16_value(b);
+  const double far = fabs(15.0 * sv + bv);
+  return fabs(sv) <= kF16Max && fabs(bv) <= kF16Max && far <= kF16Max;  // false for NaN / inf
+}
+
+bool pack_sb_row(const uint16_t* s, const uint16_t* b, int groups, uint8_t* dst) {
   for (int g = 0; g < groups; ++g) {
+    if (!group_fits_f16(s[g], b[g])) return false;
     uint32_t word = uint32_t(s[g]) | (uint32_t(b[g]) << 16);
     memcpy(dst + 4 * size_t(g), &word, 4);
   }
+  return true;
 }
 
 }  // namespace
@@ -68,9 +87,12 @@ extern "C" moe_status_t moe_pack_expert(
     if (!pack_code_row(q_gate + size_t(j) * H, H, out + L.gu_codes + size_t(rg) * (H / 2)) ||
         !pack_code_row(q_up + size_t(j) * H, H, out + L.gu_codes + size_t(ru) * (H / 2)))
       return fail(MOE_EINVAL, "moe_pack_expert: gate/up code above 15 in output row %d", j);
-    pack_sb_row(s_gate + size_t(j) * Gh, b_gate + size_t(j) * Gh, Gh,
-                out + L.gu_sb + size_t(rg) * Gh * 4);
-    pack_sb_row(s_up + size_t(j) * Gh, b_up + size_t(j) * Gh, Gh, out + L.gu_sb + size_t(ru) * Gh * 4);
+    if (!pack_sb_row(s_gate + size_t(j) * Gh, b_gate + size_t(j) * Gh, Gh,
+                     out + L.gu_sb + size_t(rg) * Gh * 4) ||
+        !pack_sb_row(s_up + size_t(j) * Gh, b_up + size_t(j) * Gh, Gh,
+                     out + L.gu_sb + size_t(ru) * Gh * 4))
+      return fail(MOE_EUNSUPPORTED, "moe_pack_expert: gate/up output row %d has a group whose "
+                  "scale, bias or 15 * scale + bias is outside the fp16 range (or not finite)", j);
     if (r > 0) {
       memcpy(out + L.b_gu + size_t(rg) * r * 2, B_gate + size_t(j) * r, size_t(r) * 2);
       memcpy(out + L.b_gu + size_t(ru) * r * 2, B_up + size_t(j) * r, size_t(r) * 2);
@@ -79,7 +101,10 @@ extern "C" moe_status_t moe_pack_expert(
   for (int i = 0; i < H; ++i) {
     if (!pack_code_row(q_down + size_t(i) * I, I, out + L.dn_codes + size_t(i) * (I / 2)))
       return fail(MOE_EINVAL, "moe_pack_expert: down code above 15 in output row %d", i);
-    pack_sb_row(s_down + size_t(i) * Gi, b_down + size_t(i) * Gi, Gi, out + L.dn_sb + size_t(i) * Gi * 4);
+    if (!pack_sb_row(s_down + size_t(i) * Gi, b_down + size_t(i) * Gi, Gi,
+                     out + L.dn_sb + size_t(i) * Gi * 4))
+      return fail(MOE_EUNSUPPORTED, "moe_pack_expert: down output row %d has a group whose "
+                  "scale, bias or 15 * scale + bias is outside the fp16 range (or not finite)", i);
   }
   if (r > 0) {
     memcpy(out + L.a_gu, A_gate, size_t(r) * H * 2);

@@ -190,6 +190,32 @@ def test_pack_rejects_codes_above_15(B):
         B.moe_pack_expert(w["H"], w["I"], w["r"], ex, blob)
 
 
+@pytest.mark.parametrize("proj,s,b,ok", [
+    ("gate", 4000.0, 0.0, True),        # 15 s = 60000: inside fp16
+    ("gate", 4400.0, 0.0, False),       # 15 s = 66000: beyond fp16
+    ("up", 1.0, -65280.0, True),        # |b| the largest bf16 inside fp16, 15 s + b inside
+    ("down", 2.0, 65500.0, False),      # 15 s + b beyond fp16
+    ("down", float("nan"), 0.0, False),
+    ("up", 0.0, float("inf"), False),
+])
+def test_pack_rejects_groups_outside_f16_range(B, proj, s, b, ok):
+    # the prefill GEMMs dequantise w = fp16(s q + b); the packer refuses
+    # groups whose weights fp16 cannot hold
+    w = synth.workload(0)
+    ex = synth.expert_tensors(w, 0, 0)
+    for k, v in ((f"s_{proj}", s), (f"b_{proj}", b)):
+        ex[k] = ex[k].copy()
+        ex[k][3, 1] = synth.f32_to_bf16_bits(np.array([v], np.float32))[0] if np.isfinite(v) else (
+            0x7FC0 if np.isnan(v) else 0x7F80)
+    blob = np.zeros(B.moe_expert_blob_bytes(w["H"], w["I"], w["r"]), np.uint8)
+    if ok:
+        B.moe_pack_expert(w["H"], w["I"], w["r"], ex, blob)
+    else:
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_pack_expert(w["H"], w["I"], w["r"], ex, blob)
+        assert ei.value.status == 2 and "fp16" in str(ei.value)
+
+
 def test_block_decode_noalloc_validates_before_device_work(B):
     # the allocation-free decode entry point checks its arguments before it
     # looks up or touches its device scratch: no GPU is needed for these
