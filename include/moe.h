@@ -297,7 +297,7 @@ MOE_API moe_status_t moe_block_decode_exec(const moe_dims_t* d, const int8_t* ga
  *   MOE_EUNSUPPORTED before any device work.  Every call on one GPU shares
  *   that GPU's array: calls that overlap in time on one GPU (different
  *   streams or threads without ordering) race and give undefined results. */
-#define MOE_NOALLOC_SCRATCH_BYTES 524288
+#define MOE_NOALLOC_SCRATCH_BYTES 1048576
 MOE_API moe_status_t moe_block_decode_noalloc(const moe_dims_t* d, const int8_t* gate_q,
                                               const float* gate_s, const int8_t* sgate_q,
                                               const float* sgate_s, const moe_experts_t* routed,

@@ -355,6 +355,7 @@ moe_status_t block_decode_launch(const char* fn, const moe_dims_t* d, const int8
   a.h = reinterpret_cast<tword_t*>(wsb + W.h);
   a.hexp = reinterpret_cast<tword_t*>(wsb + W.hexp);
   a.vpart = reinterpret_cast<tword_t*>(wsb + W.vpart);
+  a.v = reinterpret_cast<tword_t*>(wsb + W.v);
   return hip_status(launch_fused(a, static_cast<hipStream_t>(stream)), fn);
 }
 

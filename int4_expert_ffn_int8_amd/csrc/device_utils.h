@@ -138,6 +138,17 @@ __device__ __forceinline__ float wave_max(float f) {
   v = max(v, dpp_u<kDppBcast31, 0xC>(v, v));
   return f32_from_order_key(uint32_t(__builtin_amdgcn_readlane(int(v), 63)));
 }
+// Wave max of unsigned keys.  Lanes outside a row broadcast's row mask read
+// 0, the identity of max, so each step is one fused DPP instruction.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<kDppXor1>(v));
+  v = max(v, dpp_u<kDppXor2>(v));
+  v = max(v, dpp_u<kDppHalfMirror>(v));
+  v = max(v, dpp_u<kDppMirror>(v));
+  v = max(v, dpp_u<kDppBcast15, 0xA>(v));
+  v = max(v, dpp_u<kDppBcast31, 0xC>(v));
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+}
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   v = min(v, dpp_u<kDppXor1>(v));
   v = min(v, dpp_u<kDppXor2>(v));

@@ -11,7 +11,8 @@ namespace moe {
 
 constexpr int kFusedMaxT = 4;    // tokens per fused call
 constexpr int kFusedMaxP = 8;    // (token, slot) pairs per fused call
-constexpr int kFusedJW = 32;     // gate/up outputs per workgroup
+constexpr int kFusedJW = 16;     // gate/up outputs per workgroup = columns per h exponent
+constexpr int kCopies = 8;       // copies of each broadcast hand-off word (one per XCD)
 constexpr unsigned kFusedSpinLimit = 1u << 20;  // bounded waits (~0.2 s)
 
 // Control words at the start of the fused workspace, one 256-byte slot each.
@@ -48,35 +49,39 @@ struct FusedArgs {
   const int32_t* exec_idx;  // [T][K] experts to execute (prediction-as-routing) or null
   int32_t* err_out;         // device int32 or null: the last workgroup moves the sticky
                             // error word here and clears it
-  // workspace
+  // workspace; words that many workgroups read are written in kCopies copies
+  // and each reader takes the copy of its XCD (blockIdx % 8)
   int* sync;
-  tword_t* logits;  // [T][E + 1]   router logits; column E: shared-gate logit
-  tword_t* route;   // [T][K]       expert ids
-  tword_t* wts;     // [T][K + 1]   routing weights; column K: shared gate
-  tword_t* u;       // [P][2r]      A_gate x, A_up x
-  tword_t* h;       // [P][I / 2]   fp16 pairs of h * 2^-e
-  tword_t* hexp;    // [P][I / 32]  e of each 32-column block of h
-  tword_t* vpart;   // [P][I / kFusedJW][r]
+  tword_t* logits;  // [T][E + 1]                router logits; column E: shared-gate logit
+  tword_t* route;   // [kCopies][T][K]           expert ids
+  tword_t* wts;     // [kCopies][T][K + 1]       routing weights; column K: shared gate
+  tword_t* u;       // [kCopies][P][2r]          A_gate x, A_up x
+  tword_t* h;       // [kCopies][P][I / 2]       fp16 pairs of h * 2^-e
+  tword_t* hexp;    // [kCopies][P][I / JW]      e of each JW-column block of h
+  tword_t* vpart;   // [P][I / JW][r]            per-block partials of A_down h
+  tword_t* v;       // [kCopies][P][r]           A_down h
   // grid layout (filled by the launcher)
-  int nR, nWA, nBG, nD, base_la, base_gu, base_dn, total;
+  int nR, nWA, nBG, nV, nD, base_la, base_gu, base_v, base_dn, total;
 };
 
 struct FusedWs {
-  size_t sync, logits, route, wts, u, h, hexp, vpart, total;
+  size_t sync, logits, route, wts, u, h, hexp, vpart, v, total;
 };
 
 inline FusedWs fused_ws_layout(int T, int E, int K, int S, int I, int r) {
   FusedWs W;
   const size_t P = size_t(T) * (K + S);
+  const size_t C = kCopies;
   size_t o = 0;
   W.sync = o;   o = align256(o + kSyncBytes);
   W.logits = o; o = align256(o + size_t(T) * (E + 1) * 8);
-  W.route = o;  o = align256(o + size_t(T) * K * 8);
-  W.wts = o;    o = align256(o + size_t(T) * (K + 1) * 8);
-  W.u = o;      o = align256(o + P * 2 * r * 8);
-  W.h = o;      o = align256(o + P * (I / 2) * 8);
-  W.hexp = o;   o = align256(o + P * (I / 32) * 8);
+  W.route = o;  o = align256(o + C * T * K * 8);
+  W.wts = o;    o = align256(o + C * T * (K + 1) * 8);
+  W.u = o;      o = align256(o + C * P * 2 * r * 8);
+  W.h = o;      o = align256(o + C * P * (I / 2) * 8);
+  W.hexp = o;   o = align256(o + C * P * (I / kFusedJW) * 8);
   W.vpart = o;  o = align256(o + P * (I / kFusedJW) * r * 8);
+  W.v = o;      o = align256(o + C * P * r * 8);
   W.total = o;
   return W;
 }

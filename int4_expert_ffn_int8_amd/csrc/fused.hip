@@ -3,8 +3,8 @@
 // [P2] "SSD 专家卸载 · Prerouter 路由预测", decode paragraph: route, then
 // stream the chosen experts, then compute.  On MI355X a decode block moves
 // ~10 MB, which HBM delivers in ~1.3 us, while each kernel boundary costs
-// several microseconds; so the block is one kernel whose workgroups take
-// roles and hand results to each other through device memory:
+// over a microsecond; so the block is one kernel whose workgroups take roles
+// and hand results to each other through device memory:
 //
 //   router    logits of its gate rows (x = optional RMSNorm of h_in, done
 //             redundantly and identically in every workgroup); the last
@@ -14,33 +14,39 @@
 //             Prerouter bullet) it publishes those instead, weighted by the
 //             softmax of their logits.
 //   lora_a    u = [A_gate; A_up] x for one (token, slot) pair.
-//   gate_up   32 gate/up outputs of one pair (+ lambda B u), SwiGLU -> h
-//             (fp16), and that block's partial of v = A_down h.
-//   down      a block of output rows for every pair: v = sum of the pair's
-//             partials (fixed order), y = deq(Q_down) h + lambda B_down v,
-//             then the weighted combine (+ residual) -> out.
+//   gate_up   16 gate/up outputs of one pair (+ lambda B u), SwiGLU -> h
+//             (fp16 with one power-of-two exponent per 16 columns), and that
+//             block's partial of v = A_down h.
+//   vred      v = sum of a pair's partials, in block order.
+//   down      a few output rows for every pair: y = deq(Q_down) h +
+//             lambda B_down v, then the weighted combine (+ residual) -> out.
 //
 // Weight loads are issued before the waits they do not depend on (shared
 // expert from the start, routed experts as soon as their ids arrive).  An
 // expert that is not resident in the pool is read from the pinned host copy,
-// after an optional modeled storage latency (a bounded wall-clock wait).  A role
-// waits only on roles with lower workgroup ids, which the dispatcher starts
-// first, and every wait is bounded: on timeout the kernel records an error
-// and still runs to completion.
+// after an optional modeled storage latency (a bounded wall-clock wait, once
+// per workgroup).  A role waits only on roles with lower workgroup ids, which
+// the dispatcher starts first, and every wait is bounded: on timeout the
+// kernel records an error and still runs to completion.
 //
 // Hand-off protocol.  The 8 XCDs have separate L2 caches, and a device-scope
 // release/acquire fence writes back / invalidates a whole L2, which at one
 // fence per workgroup costs far more than the block itself.  So every value
 // one workgroup hands to another is a 64-bit word -- payload in the low half,
 // the launch's tag in the high half -- written and read with device-scope
-// relaxed atomics (sc1 stores and loads that the XCD L2s do not hold
-// incoherently).  A producer just stores; a consumer polls one word (from one
-// thread, with sleeps, so waiting costs little bandwidth), then loads every
-// word it needs and repeats the loads until all of them carry this launch's
-// tag.  The tag is the launch epoch + 1; the last workgroup to finish bumps
-// the epoch, so stale words of earlier launches never match and nothing needs
-// clearing.  Weights and inputs, read-only in the kernel, use ordinary cached
-// loads.
+// relaxed atomics (loads and stores that bypass the XCD L2s).  A producer just
+// stores; a consumer loads every word it needs and repeats the loads until all
+// of them carry this launch's tag.  The tag is the launch epoch + 1; the last
+// workgroup to finish bumps the epoch, so stale words of earlier launches
+// never match and nothing needs clearing.  Weights and inputs, read-only in
+// the kernel, use ordinary cached loads.
+//
+// Such loads are served at the memory side, so hundreds of workgroups
+// re-reading one word serialise there.  Words read by many workgroups
+// (routes, weights, u, h and its exponents, v) are therefore written in 8
+// copies and each reader takes the copy of its XCD; the down role first waits
+// for one word per h block from a single wave, then reads its h words once,
+// instead of polling all of them from every thread.
 //
 // Load discipline.  Vector loads complete in order, so a load whose value is
 // used inside a divergent branch makes the wave wait for every load issued
@@ -52,6 +58,12 @@
 #include "launch.h"
 #include "moe_internal.h"
 #include "topk.h"
+
+// Timeline marks: a timing build of this file defines FUSED_MARK(k) to record
+// the wall clock of a workgroup's phases; here they are empty.
+#ifndef FUSED_MARK
+#define FUSED_MARK(k)
+#endif
 
 namespace moe {
 
@@ -78,6 +90,10 @@ __device__ __forceinline__ tword_t tw(unsigned tag, uint32_t bits) {
 __device__ __forceinline__ tword_t twf(unsigned tag, float v) { return tw(tag, __float_as_uint(v)); }
 __device__ __forceinline__ bool has_tag(tword_t w, unsigned tag) { return unsigned(w >> 32) == tag; }
 __device__ __forceinline__ float wf(tword_t w) { return __uint_as_float(uint32_t(w)); }
+
+// the copy of broadcast words this workgroup reads: its XCD's (workgroups
+// are spread over the 8 XCDs round-robin by id)
+__device__ __forceinline__ int xcd_copy() { return int(blockIdx.x) & (kCopies - 1); }
 
 __device__ __forceinline__ void set_err(const FusedArgs& a) { st_dev(slot(a, kSlotErr), 1); }
 
@@ -149,7 +165,8 @@ __device__ __forceinline__ const uint8_t* expert_blob(const FusedArgs& a, int e,
 __device__ __forceinline__ int wait_expert(const FusedArgs& a, int p, unsigned tag, int* lds_int) {
   const int KS = a.K + a.S;
   if (threadIdx.x == 0)
-    *lds_int = int(uint32_t(poll_word(a, &a.route[(p / KS) * a.K + p % KS], tag)));
+    *lds_int = int(uint32_t(poll_word(
+        a, &a.route[(xcd_copy() * a.T + p / KS) * a.K + p % KS], tag)));
   __syncthreads();
   return *lds_int;
 }
@@ -187,18 +204,15 @@ __device__ __forceinline__ void token_slice(const FusedArgs& a, int t, int sub, 
   xs = s;
 }
 
-// (s*q + b) . v over the lane's 32 columns; v is bf16 (F16 false) or fp16
-template <bool F16>
-__device__ __forceinline__ float slice_dot(const uint4 q, uint32_t sbw, const uint32_t* xw,
-                                           float xs) {
+// (s*q + b) . x over the lane's 32 columns of bf16 x
+__device__ __forceinline__ float slice_dot_bf16(const uint4 q, uint32_t sbw, const uint32_t* xw,
+                                                float xs) {
   const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
   float acc = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      acc = F16 ? dot2_f16(codes_to_f16x2_biased(qw[d], s), xw[4 * d + s], acc)
-                : dot2_bf16(codes_to_bf16x2_biased(qw[d], s), xw[4 * d + s], acc);
+    for (int s = 0; s < 4; ++s) acc = dot2_bf16(codes_to_bf16x2_biased(qw[d], s), xw[4 * d + s], acc);
   const float sc = bf16_lo(sbw), bi = bf16_hi(sbw);
   return fmaf(sc, acc, (bi - 128.0f * sc) * xs);
 }
@@ -231,23 +245,25 @@ __device__ void route_token(const FusedArgs& a, int t, int lane, unsigned tag) {
     }
     __builtin_amdgcn_s_sleep(2);
   }
-  float first = 0.f, denom = 0.f, mine = 0.f;
+  if (t == 0) FUSED_MARK(2);
+  // Lane l holds slot k = l % 8 of the selection (K <= 8 here): every group
+  // of 8 lanes computes the weights, and group c publishes copy c.
+  const int kk = lane & 7;
+  float first = 0.f, mine_l = -INFINITY;
   int mine_e = 0;
   if (a.exec_idx == nullptr) {
     topk_wave(v, a.E, a.K, lane, [&](int k, float mx, uint32_t sel) {
-      if (k == 0) first = mx;
-      const float ev = expf(mx - first);
-      denom += ev;
-      if (k == lane) {
-        mine = ev;
+      if (k == 0) first = mx;  // the largest logit
+      if (k == kk) {
+        mine_l = mx;
         mine_e = int(sel);
       }
     });
   } else {
-    // given experts: lane k < K takes expert exec_idx[t][k] and fetches its
-    // logit from the lane that holds it
-    if (lane < a.K) {
-      mine_e = a.exec_idx[t * a.K + lane];
+    // given experts: slot k takes expert exec_idx[t][k] and fetches its logit
+    // from the lane that holds it
+    if (kk < a.K) {
+      mine_e = a.exec_idx[t * a.K + kk];
       if (uint32_t(mine_e) >= uint32_t(a.E)) {
         set_err(a);
         mine_e = 0;
@@ -260,36 +276,38 @@ __device__ void route_token(const FusedArgs& a, int t, int lane, unsigned tag) {
       const float c = __shfl(v[m], mine_e & 63);
       if ((mine_e >> 6) == m) gl = c;
     }
-    first = wave_max(lane < a.K ? gl : -INFINITY);
-    mine = lane < a.K ? expf(gl - first) : 0.f;
-    // summed in k order, as the selection path does: given experts equal
-    // to the router's top-K reproduce its weights bit for bit
-    for (int k = 0; k < a.K; ++k) denom += __shfl(mine, k);
-    if (!a.norm_topk) {  // the full-softmax form below subtracts the largest logit
-      float mx = -INFINITY;
-#pragma unroll
-      for (int m = 0; m < MP; ++m)
-        if (lane + 64 * m < a.E) mx = fmaxf(mx, v[m]);
-      const float top = wave_max(mx);
-      mine = lane < a.K ? expf(gl - top) : 0.f;
-      first = top;
-    }
+    mine_l = kk < a.K ? gl : -INFINITY;
+    first = wave_max(mine_l);
   }
-  if (!a.norm_topk) {  // full-softmax entries: denominator over all E
+  float mine = kk < a.K ? expf(mine_l - first) : 0.f;
+  float denom;
+  if (a.norm_topk) {
+    denom = group_sum<8>(mine);  // fixed pairing: the same bits on every path
+  } else {  // full-softmax entries: denominator over all E, from the largest logit
+    float mx = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < MP; ++m)
+      if (lane + 64 * m < a.E) mx = fmaxf(mx, v[m]);
+    const float top = wave_max(mx);
+    mine = kk < a.K ? expf(mine_l - top) : 0.f;
     float part = 0.f;
 #pragma unroll
     for (int m = 0; m < MP; ++m)
-      if (lane + 64 * m < a.E) part += expf(v[m] - first);
+      if (lane + 64 * m < a.E) part += expf(v[m] - top);
     denom = group_sum<64>(part);
   }
+  const float wv = mine / denom;
   if (lane < a.K) {
-    const float wv = mine / denom;
-    st_dev(&a.route[t * a.K + lane], tw(tag, uint32_t(mine_e)));
-    st_dev(&a.wts[t * (a.K + 1) + lane], twf(tag, wv));
     if (a.user_idx) a.user_idx[t * a.K + lane] = mine_e;
     if (a.user_w) a.user_w[t * a.K + lane] = wv;
   }
-  if (a.S && lane == 0) st_dev(&a.wts[t * (a.K + 1) + a.K], twf(tag, sigmoid_f(sgl)));
+  const int c = lane >> 3;
+  if (kk < a.K) {
+    st_dev(&a.route[(c * a.T + t) * a.K + kk], tw(tag, uint32_t(mine_e)));
+    st_dev(&a.wts[(c * a.T + t) * (a.K + 1) + kk], twf(tag, wv));
+  }
+  if (a.S && kk == 0) st_dev(&a.wts[(c * a.T + t) * (a.K + 1) + a.K], twf(tag, sigmoid_f(sgl)));
+  if (t == 0) FUSED_MARK(3);
 }
 
 template <int H>
@@ -327,6 +345,7 @@ __device__ void role_router(const FusedArgs& a, int b) {
     // column E of the logits row holds the shared-gate logit
     if (valid && sub == 0) st_dev(&a.logits[t * (a.E + 1) + row], twf(tag, part));
   }
+  FUSED_MARK(1);
   if (b != a.nR - 1) return;
   // The last router workgroup: wait for every logit of its token (one wave
   // per token), then K rounds of wave argmax by (logit desc, index asc).
@@ -345,6 +364,7 @@ __device__ void role_lora_a(const FusedArgs& a, int unit, int part, int* lds_int
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane % G::LPR;
   const int p = pair_of_unit(a, unit);
   const int KS = a.K + a.S;
+  const int P = a.T * KS;
   const int t = p / KS;
   const bool routed = (p % KS) < a.K;
   const unsigned tag = launch_tag(a);
@@ -353,6 +373,7 @@ __device__ void role_lora_a(const FusedArgs& a, int unit, int part, int* lds_int
   token_slice<H>(a, t, sub, xw, xs);
   const uint8_t* blob = a.shared_blob;
   if (routed) blob = expert_blob(a, wait_expert(a, p, tag, lds_int), false);
+  FUSED_MARK(1);
   const uint16_t* A = reinterpret_cast<const uint16_t*>(blob + a.L.a_gu);
   const int rows = 2 * a.r;
   const int rw = part * 4 * G::RPL + wave * G::RPL + lane / G::LPR;  // 4 waves x RPL rows
@@ -368,8 +389,10 @@ __device__ void role_lora_a(const FusedArgs& a, int unit, int part, int* lds_int
     acc = dot2_bf16(q[k].z, xw[4 * k + 2], acc);
     acc = dot2_bf16(q[k].w, xw[4 * k + 3], acc);
   }
-  acc = group_sum<G::LPR>(acc);
-  if (rw < rows && sub == 0) st_dev(&a.u[p * rows + rw], twf(tag, acc));
+  acc = group_sum<G::LPR>(acc);  // every lane of the row group holds the sum
+  static_assert(Geo<256>::LPR >= kCopies, "one lane per copy");
+  if (rw < rows && sub < kCopies) st_dev(&a.u[(sub * P + p) * rows + rw], twf(tag, acc));
+  FUSED_MARK(2);
 }
 
 // ---------------------------------------------------------------------------
@@ -380,10 +403,13 @@ __device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, 
   constexpr int JW = kFusedJW, JPW = JW / 4;  // outputs per workgroup / wave
   constexpr int NR = 2 * JPW, NL = NR / RPL;  // gate + up rows per wave, loads per lane
   static_assert(NR % RPL == 0, "rows per wave");
+  static_assert(JW * kMaxR == 256, "one (rank, column) product of v per thread");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane % G::LPR;
   const int tid = threadIdx.x;
   const int p = pair_of_unit(a, unit);
   const int KS = a.K + a.S;
+  const int P = a.T * KS;
+  const int NB = a.I / JW;
   const int t = p / KS;
   const bool routed = (p % KS) < a.K;
   const int j0 = blk * JW + wave * JPW;
@@ -391,6 +417,7 @@ __device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, 
   const unsigned tag = launch_tag(a);
   const uint8_t* blob = a.shared_blob;
   if (routed) blob = expert_blob(a, wait_expert(a, p, tag, lds_int), false);
+  FUSED_MARK(1);
   // every weight this workgroup needs, before anything waits on data
   const uint8_t* codes = blob + a.L.gu_codes;
   const uint32_t* sb = reinterpret_cast<const uint32_t*>(blob + a.L.gu_sb);
@@ -400,7 +427,7 @@ __device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, 
   uint32_t sbw[NL];
   int brow[NL];
   uint16_t braw[NL];  // B[row][sub] (one LoRA rank per lane; r <= LPR)
-  uint16_t adraw[2];  // A_down entries of this block's partial of v
+  uint16_t adraw = 0; // A_down[rank tid / JW][column blk * JW + tid % JW]
   const int rc = max(r - 1, 0);
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
@@ -413,30 +440,30 @@ __device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, 
   if (r > 0) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) braw[i] = Bgu[size_t(brow[i]) * r + min(sub, rc)];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int id = c * 256 + tid, rr = min(id / JW, rc), jj = id % JW;
-      adraw[c] = Ad[size_t(rr) * a.I + blk * JW + jj];
-    }
+    adraw = Ad[size_t(min(tid / JW, rc)) * a.I + blk * JW + tid % JW];
   }
   uint32_t xw[16];
   float xs;
   token_slice<H>(a, t, sub, xw, xs);
   float part[NL];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) part[i] = slice_dot<false>(q[i], sbw[i], xw, xs);
+  for (int i = 0; i < NL; ++i) part[i] = slice_dot_bf16(q[i], sbw[i], xw, xs);
+  FUSED_MARK(2);
   float* lds_a = lds;           // [4][NR]
   float* lds_h = lds + 4 * NR;  // [JW]
+  float* lds_hraw = lds_h + JW; // [JW]
   if (r > 0) {  // u = A x of this pair (from its lora_a workgroups)
+    const tword_t* up = a.u + (size_t(xcd_copy()) * P + p) * 2 * r;
     float uv[2] = {0.f, 0.f};  // lane's rank `sub` of A_gate x and A_up x
     for (unsigned n = 0;; ++n) {
-      const tword_t g = ld_dev(&a.u[p * 2 * r + min(sub, rc)]);
-      const tword_t uu = ld_dev(&a.u[p * 2 * r + r + min(sub, rc)]);
+      const tword_t g = ld_dev(&up[min(sub, rc)]);
+      const tword_t uu = ld_dev(&up[r + min(sub, rc)]);
       const bool ok = has_tag(g, tag) && has_tag(uu, tag);
       uv[0] = wf(g);
       uv[1] = wf(uu);
       if (round_done(a, ok, n)) break;
     }
+    FUSED_MARK(3);
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int ri = i * RPL + lane / G::LPR;
@@ -447,79 +474,180 @@ __device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, 
   // all sums first (independent chains interleave), then the stores
 #pragma unroll
   for (int i = 0; i < NL; ++i) part[i] = group_sum<G::LPR>(part[i]);
-  if (sub == 0) {
+  int hexp;
+  if constexpr (RPL == 1) {
+    // each wave holds all rows of its JPW outputs in every lane: SwiGLU in
+    // registers, one barrier to share the raw h and the wave maxima
+    float hv[JPW], wmax = 0.f;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) lds_a[wave * NR + i * RPL + lane / G::LPR] = part[i];
-  }
-  __syncthreads();
-  float* lds_hraw = lds_h + JW;  // [JW]
-  if (tid < JW) {
-    const int w = tid / JPW, jl = tid % JPW;
-    lds_hraw[tid] = silu_f(lds_a[w * NR + 2 * jl]) * lds_a[w * NR + 2 * jl + 1];
-  }
-  __syncthreads();
-  // this block of h is one 32-column slice of the down rows: it is stored as
-  // fp16(h * 2^-e) with one exponent e per block (e = 0 unless |h| >= 2^15)
-  float hmax = 0.f;
-  for (int j = 0; j < JW; ++j) hmax = fmaxf(hmax, fabsf(lds_hraw[j]));
-  const int hexp = h_block_exp(hmax);
-  if (tid < JW) lds_h[tid] = ldexpf(f16_to_f32(f32_to_f16_sat(ldexpf(lds_hraw[tid], -hexp))), hexp);
-  __syncthreads();
-  if (tid < JW / 2) {  // fp16 pairs of h * 2^-e, one tagged word per pair
-    f16x2_t pr = {_Float16(ldexpf(lds_h[2 * tid], -hexp)), _Float16(ldexpf(lds_h[2 * tid + 1], -hexp))};
-    st_dev(&a.h[p * (a.I / 2) + blk * (JW / 2) + tid], tw(tag, __builtin_bit_cast(uint32_t, pr)));
-  } else if (tid == JW / 2) {
-    st_dev(&a.hexp[p * (a.I / JW) + blk], tw(tag, uint32_t(hexp)));
-  }
-  if (r > 0) {  // this block's partial of v = A_down h
-    const int NB = a.I / JW;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int id = c * 256 + tid, rr = id / JW, jj = id % JW;
-      const float ad = (rr < r) ? bf16_to_f32(adraw[c]) : 0.f;
-      const float prod = group_sum<JW>(ad * lds_h[jj]);
-      if (jj == 0 && rr < r) st_dev(&a.vpart[(p * NB + blk) * r + rr], twf(tag, prod));
+    for (int jl = 0; jl < JPW; ++jl) {
+      hv[jl] = silu_f(part[2 * jl]) * part[2 * jl + 1];
+      wmax = fmaxf(wmax, fabsf(hv[jl]));
     }
+    if (lane < JPW) {
+      float hl = hv[0];
+#pragma unroll
+      for (int jl = 1; jl < JPW; ++jl)
+        if (lane == jl) hl = hv[jl];
+      lds_hraw[wave * JPW + lane] = hl;
+    }
+    if (lane == 0) lds_a[wave] = wmax;
+    __syncthreads();
+    // this block of h is one 16-column slice of the down rows: it is stored
+    // as fp16(h * 2^-e) with one exponent e per block (e = 0 unless |h| >= 2^15)
+    hexp = h_block_exp(fmaxf(fmaxf(lds_a[0], lds_a[1]), fmaxf(lds_a[2], lds_a[3])));
+    // every copy: lanes 2c + i of wave w store word 2w + i (outputs 4w + 2i,
+    // 4w + 2i + 1) of copy c
+    if (lane < 2 * kCopies) {
+      const int i = lane & 1, c = lane >> 1;
+      const float h0 = i ? hv[2] : hv[0], h1 = i ? hv[3] : hv[1];
+      const f16x2_t pr = {_Float16(f16_to_f32(f32_to_f16_sat(ldexpf(h0, -hexp)))),
+                          _Float16(f16_to_f32(f32_to_f16_sat(ldexpf(h1, -hexp))))};
+      st_dev(&a.h[(size_t(c) * P + p) * (a.I / 2) + blk * (JW / 2) + 2 * wave + i],
+             tw(tag, __builtin_bit_cast(uint32_t, pr)));
+    } else if (wave == 0 && lane >= 32 && lane < 32 + kCopies) {
+      st_dev(&a.hexp[(size_t(lane - 32) * P + p) * NB + blk], tw(tag, uint32_t(hexp)));
+    }
+    // the block's h as the down rows will see it, for the v partial
+    if (tid < JW)
+      lds_h[tid] = ldexpf(f16_to_f32(f32_to_f16_sat(ldexpf(lds_hraw[tid], -hexp))), hexp);
+    __syncthreads();
+  } else {
+    if (sub == 0) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) lds_a[wave * NR + i * RPL + lane / G::LPR] = part[i];
+    }
+    __syncthreads();
+    if (tid < JW) {
+      const int w = tid / JPW, jl = tid % JPW;
+      lds_hraw[tid] = silu_f(lds_a[w * NR + 2 * jl]) * lds_a[w * NR + 2 * jl + 1];
+    }
+    __syncthreads();
+    // this block of h is one 16-column slice of the down rows: it is stored as
+    // fp16(h * 2^-e) with one exponent e per block (e = 0 unless |h| >= 2^15)
+    float hmax = 0.f;
+#pragma unroll
+    for (int j = 0; j < JW; ++j) hmax = fmaxf(hmax, fabsf(lds_hraw[j]));
+    hexp = h_block_exp(hmax);
+    if (tid < JW) lds_h[tid] = ldexpf(f16_to_f32(f32_to_f16_sat(ldexpf(lds_hraw[tid], -hexp))), hexp);
+    __syncthreads();
+    // every copy: fp16 pairs of h * 2^-e (one tagged word per pair), then e
+    if (tid < kCopies * (JW / 2)) {
+      const int c = tid / (JW / 2), i = tid % (JW / 2);
+      const f16x2_t pr = {_Float16(ldexpf(lds_h[2 * i], -hexp)), _Float16(ldexpf(lds_h[2 * i + 1], -hexp))};
+      st_dev(&a.h[(size_t(c) * P + p) * (a.I / 2) + blk * (JW / 2) + i],
+             tw(tag, __builtin_bit_cast(uint32_t, pr)));
+    } else if (tid >= 64 && tid < 64 + kCopies) {
+      st_dev(&a.hexp[(size_t(tid - 64) * P + p) * NB + blk], tw(tag, uint32_t(hexp)));
+    }
+  }
+  FUSED_MARK(4);
+  if (r > 0) {  // this block's partial of v = A_down h: thread (rank, column)
+    const int rr = tid / JW, jj = tid % JW;
+    const float ad = (rr < r) ? bf16_to_f32(adraw) : 0.f;
+    const float prod = group_sum<JW>(ad * lds_h[jj]);
+    if (jj == 0 && rr < r) st_dev(&a.vpart[(size_t(p) * NB + blk) * r + rr], twf(tag, prod));
   }
 }
 
 // ---------------------------------------------------------------------------
+// v of one pair: its NB blocks' partials of A_down h.  Thread (rank tid % 16,
+// group tid / 16) adds blocks group, group + 16, ... in order; the 16 group
+// sums of a rank are then added in group order (a fixed order: the same bits
+// every launch).
+template <int I>
+__device__ void role_vred(const FusedArgs& a, int unit, float* lds) {
+  constexpr int NB = I / kFusedJW;
+  constexpr int NBG = (NB + 15) / 16;  // blocks per thread
+  static_assert(kMaxR == 16, "one rank per lane of a 16-lane group");
+  const int tid = threadIdx.x;
+  const int rr = tid & 15, bg = tid >> 4;
+  const int p = pair_of_unit(a, unit);
+  const int P = a.T * (a.K + a.S);
+  const int r = a.r;
+  const unsigned tag = launch_tag(a);
+  const tword_t* vp = a.vpart + size_t(p) * NB * r;
+  const int rc = min(rr, r - 1);
+  tword_t w[NBG];
+  for (unsigned it = 0;; ++it) {
+#pragma unroll
+    for (int k = 0; k < NBG; ++k) w[k] = ld_dev(&vp[min(bg + 16 * k, NB - 1) * r + rc]);
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < NBG; ++k) ok &= (bg + 16 * k >= NB) || (rr >= r) || has_tag(w[k], tag);
+    if (round_done(a, ok, it)) break;
+  }
+  FUSED_MARK(1);
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < NBG; ++k)
+    if (bg + 16 * k < NB) sum += wf(w[k]);
+  lds[bg * 16 + rr] = sum;
+  __syncthreads();
+  if (tid < r * kCopies) {
+    const int c = tid / r, k = tid % r;
+    float v = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) v += lds[g * 16 + k];  // groups past NB hold 0
+    st_dev(&a.v[(size_t(c) * P + p) * r + k], twf(tag, v));
+  }
+  FUSED_MARK(2);
+}
+
+// ---------------------------------------------------------------------------
+// Down rows: each lane owns SL slices of kFusedJW (16) columns of its row,
+// i.e. whole h exponent blocks.
+template <int I>
+struct DGeo {
+  static constexpr int NS = I / kFusedJW;           // slices per row
+  static constexpr int LPR = NS < 64 ? NS : 64;     // lanes per row
+  static constexpr int RPL = 64 / LPR;              // rows per wave
+  static constexpr int SL = NS / LPR;               // slices per lane
+  static_assert(NS % LPR == 0 && SL >= 1, "down geometry");
+};
+
 template <int H, int I>
 __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* lds_hs, int* lds_he,
-                          float* lds_v,
-                          float* lds_wt, int* lds_idx) {
-  using G = Geo<I>;
-  constexpr int RPL = G::RPL;
-  constexpr int NB = I / kFusedJW;  // partials of A_down h per pair
-  constexpr int MAXH = (kFusedMaxP * I / 2 + 255) / 256;
-  constexpr int MAXC = (kFusedMaxP * kMaxR * 16 + 255) / 256;
-  constexpr int MAXE = (kFusedMaxP * I / 32 + 255) / 256;
-  static_assert(kFusedJW == 32, "one h exponent per 32-column slice of a down row");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane % G::LPR;
+                          float* lds_v, float* lds_wt, int* lds_idx) {
+  using D = DGeo<I>;
+  constexpr int LPR = D::LPR, SL = D::SL;
+  constexpr int NB = I / kFusedJW;                      // h blocks per pair
+  constexpr int MAXH = (kFusedMaxP * I / 2 + 255) / 256;  // h words per thread
+  constexpr int MAXE = (kFusedMaxP * NB + 255) / 256;     // exponents per thread
+  constexpr int MAXCAN = (kFusedMaxP * NB + 63) / 64;     // exponents per lane of the canary wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane % LPR;
   const int tid = threadIdx.x;
-  const int row = d * 4 * RPL + wave * RPL + lane / G::LPR;
+  const int row = d * 4 * D::RPL + wave * D::RPL + lane / LPR;
   const bool valid = row < H;
   const int KS = a.K + a.S;
   const int P = a.T * KS;
   const int r = a.r;
+  const int c = xcd_copy();
   const unsigned tag = launch_tag(a);
-  // Prefetch this lane's down-row slice of every pair into registers: the
+  // Prefetch this lane's down-row slices of every pair into registers: the
   // shared expert at once, routed experts as soon as their ids arrive.
-  uint4 q[kFusedMaxP];
-  uint32_t sbw[kFusedMaxP];
+  uint2 q[kFusedMaxP][SL];
+  uint32_t sbw[kFusedMaxP][SL];
   uint16_t bdraw[kFusedMaxP];  // B_down[row][sub]
   const uint8_t* bl[kFusedMaxP];
   const int rowc = min(row, H - 1), subr = min(sub, max(r - 1, 0));
   auto fetch = [&](int p) {  // p is workgroup-uniform: no divergent guard
-    q[p] = *reinterpret_cast<const uint4*>(bl[p] + a.L.dn_codes + size_t(rowc) * (I / 2) + 16 * sub);
-    sbw[p] = reinterpret_cast<const uint32_t*>(bl[p] + a.L.dn_sb)[size_t(rowc) * (I / 64) + (sub >> 1)];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int sl = sub + LPR * s;
+      q[p][s] = *reinterpret_cast<const uint2*>(bl[p] + a.L.dn_codes + size_t(rowc) * (I / 2) + 8 * sl);
+      sbw[p][s] = reinterpret_cast<const uint32_t*>(bl[p] + a.L.dn_sb)[size_t(rowc) * (I / 64) + sl / 4];
+    }
     if (r > 0)
       bdraw[p] = reinterpret_cast<const uint16_t*>(bl[p] + a.L.b_dn)[size_t(rowc) * r + subr];
   };
 #pragma unroll
   for (int p = 0; p < kFusedMaxP; ++p) {
-    q[p] = make_uint4(0, 0, 0, 0);
-    sbw[p] = 0;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      q[p][s] = make_uint2(0, 0);
+      sbw[p][s] = 0;
+    }
     bdraw[p] = 0;
     bl[p] = a.shared_blob;
     if (p < P && (p % KS) >= a.K) fetch(p);
@@ -531,9 +659,11 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
   // routed expert ids: one polling thread per pair
   if (tid < P) {
     const int t = tid / KS, k = tid % KS;
-    lds_idx[tid] = (k < a.K) ? int(uint32_t(poll_word(a, &a.route[t * a.K + k], tag))) : -1;
+    lds_idx[tid] =
+        (k < a.K) ? int(uint32_t(poll_word(a, &a.route[(c * a.T + t) * a.K + k], tag))) : -1;
   }
   __syncthreads();
+  FUSED_MARK(1);
   // resident blobs are fetched at once; if any blob is the host copy, one
   // modeled latency precedes all of this thread's host reads
   uint32_t missed = 0;
@@ -554,117 +684,126 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
     for (int p = 0; p < kFusedMaxP; ++p)
       if ((missed >> p) & 1u) fetch(p);
   }
-  // wait for the last h word, then load every pair's h, v partials and
-  // routing weights until all carry this launch's tag
-  if (tid == 0) poll_word(a, &a.h[P * (I / 2) - 1], tag);
-  __syncthreads();
-  tword_t hv[MAXH], vp[MAXC];
-  float wtv = 0.f;
-  const int nh = P * (I / 2);
-  const int ne = P * (I / 32);
-  tword_t hev[MAXE];
-  const int tw_t = min(tid, P - 1) / KS, tw_k = min(tid, P - 1) % KS;
-  const int tw_i = tw_t * (a.K + 1) + (tw_k < a.K ? tw_k : a.K);
-  // partial of v read by slot c of this thread: (pair, rank, block < 16);
-  // without LoRA every slot reads a valid dummy word and is not checked
-  const tword_t* vsrc = (r > 0) ? a.vpart : a.wts;
-  int vidx[MAXC];
-  uint32_t vneed = 0;
+  // One wave waits until every h block of every pair has published its
+  // exponent (each block writes it with its h words)...
+  const int nblk = P * NB;
+  const tword_t* hexp_c = a.hexp + size_t(c) * P * NB;
+  if (wave == 0) {
+    for (unsigned n = 0;; ++n) {
+      tword_t cw[MAXCAN];
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    const int id = c * 256 + tid;
-    const int pr = id >> 4, q16 = id & 15;
-    const int p = (r > 0) ? pr / r : P, rr = (r > 0) ? pr % r : 0;
-    const bool need = p < P && q16 < NB;  // NB <= 16 here; larger NB is summed below
-    vidx[c] = need ? (p * NB + q16) * r + rr : 0;
-    vneed |= uint32_t(need) << c;
+      for (int k = 0; k < MAXCAN; ++k) cw[k] = ld_dev(&hexp_c[min(lane + 64 * k, nblk - 1)]);
+      bool ok = true;
+#pragma unroll
+      for (int k = 0; k < MAXCAN; ++k) ok &= (lane + 64 * k >= nblk) || has_tag(cw[k], tag);
+      if (__all(ok)) break;
+      if (++n > kFusedSpinLimit) {
+        if (lane == 0) set_err(a);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
   }
+  __syncthreads();
+  FUSED_MARK(2);
+  // ...then the workgroup reads h, the exponents and the routing weights,
+  // repeating the reads until every word carries this launch's tag
+  const tword_t* h_c = a.h + size_t(c) * P * (I / 2);
+  const int nh = P * (I / 2);
+  tword_t hv[MAXH], hev[MAXE];
+  float wtv = 0.f;
+  const int tw_t = min(tid, P - 1) / KS, tw_k = min(tid, P - 1) % KS;
+  const int tw_i = (c * a.T + tw_t) * (a.K + 1) + (tw_k < a.K ? tw_k : a.K);
   for (unsigned n = 0;; ++n) {
-    // every load of the round first (fixed count, clamped indices), then the checks
 #pragma unroll
-    for (int k = 0; k < MAXH; ++k) hv[k] = ld_dev(&a.h[min(tid + 256 * k, nh - 1)]);
+    for (int k = 0; k < MAXH; ++k) hv[k] = ld_dev(&h_c[min(tid + 256 * k, nh - 1)]);
 #pragma unroll
-    for (int k = 0; k < MAXE; ++k) hev[k] = ld_dev(&a.hexp[min(tid + 256 * k, ne - 1)]);
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) vp[c] = ld_dev(&vsrc[vidx[c]]);
+    for (int k = 0; k < MAXE; ++k) hev[k] = ld_dev(&hexp_c[min(tid + 256 * k, nblk - 1)]);
     const tword_t w = ld_dev(&a.wts[tw_i]);
     unsigned bad = unsigned(tid < P) & unsigned(!has_tag(w, tag));
     wtv = wf(w);
 #pragma unroll
     for (int k = 0; k < MAXH; ++k) bad |= unsigned(tid + 256 * k < nh) & unsigned(!has_tag(hv[k], tag));
 #pragma unroll
-    for (int k = 0; k < MAXE; ++k) bad |= unsigned(tid + 256 * k < ne) & unsigned(!has_tag(hev[k], tag));
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) bad |= ((vneed >> c) & 1u) & unsigned(!has_tag(vp[c], tag));
+    for (int k = 0; k < MAXE; ++k)
+      bad |= unsigned(tid + 256 * k < nblk) & unsigned(!has_tag(hev[k], tag));
     if (round_done(a, bad == 0, n)) break;
   }
-  // partial blocks beyond the first 16 (I > 512): summed after the round
-  float vs[MAXC];
-#pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    const int id = c * 256 + tid;
-    const int pr = id >> 4, q16 = id & 15;
-    const int p = (r > 0) ? pr / r : P, rr = (r > 0) ? pr % r : 0;
-    float s = ((vneed >> c) & 1u) ? wf(vp[c]) : 0.f;
-    if (p < P)
-      for (int bb = q16 + 16; bb < NB; bb += 16) {
-        const tword_t w = poll_word(a, &a.vpart[(p * NB + bb) * r + rr], tag);
-        s += wf(w);
-      }
-    vs[c] = s;
-  }
+  FUSED_MARK(3);
+  // v of every pair (copy c): loaded now, so its latency overlaps the work
+  // below; checked (and reloaded if not yet published) before its use
+  const int nv = P * r;
+  const tword_t* v_c = a.v + size_t(c) * P * r;
+  tword_t vw = 0;
+  if (r > 0) vw = ld_dev(&v_c[min(tid, nv - 1)]);
   {
-    // h words to LDS, and the sum of each 32-column slice (16 consecutive
-    // words, held by 16 consecutive threads) for the affine term
+    // h words to LDS, and the sum of each 16-column block (8 consecutive
+    // words, held by 8 consecutive threads) for the affine term
     uint32_t* dst = reinterpret_cast<uint32_t*>(lds_hh);
 #pragma unroll
     for (int k = 0; k < MAXH; ++k) {
       const int i = tid + 256 * k;
       const uint32_t hw = uint32_t(hv[k]);
-      const float ss = group_sum<16>(f16_lo(hw) + f16_hi(hw));
+      const float ss = group_sum<8>(f16_lo(hw) + f16_hi(hw));
       if (i < nh) {
         dst[i] = hw;
-        if ((i & 15) == 0) lds_hs[i >> 4] = ss;
+        if ((i & 7) == 0) lds_hs[i >> 3] = ss;
       }
-    }
-  }
-  if (r > 0) {
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      const int id = c * 256 + tid;
-      const int pr = id >> 4, q16 = id & 15;
-      const int p = pr / r, rr = pr % r;
-      const float s = group_sum<16>(vs[c]);
-      if (q16 == 0 && p < P) lds_v[p * kMaxR + rr] = s;
     }
   }
   if (tid < P) lds_wt[tid] = wtv;
 #pragma unroll
   for (int k = 0; k < MAXE; ++k)
-    if (tid + 256 * k < ne) lds_he[tid + 256 * k] = int(uint32_t(hev[k]));
+    if (tid + 256 * k < nblk) lds_he[tid + 256 * k] = int(uint32_t(hev[k]));
   __syncthreads();
+  // this lane's part of every pair's output row
+  float y[kFusedMaxP];
+#pragma unroll
+  for (int p = 0; p < kFusedMaxP; ++p) {
+    y[p] = 0.f;
+    if (p >= P) continue;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int sl = sub + LPR * s;  // block of 16 columns
+      const uint4* hp = reinterpret_cast<const uint4*>(lds_hh + p * I + 16 * sl);
+      const uint4 h0 = hp[0], h1 = hp[1];
+      const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+      const uint32_t qw[2] = {q[p][s].x, q[p][s].y};
+      float acc = 0.f;
+#pragma unroll
+      for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) acc = dot2_f16(codes_to_f16x2_biased(qw[dd], s4), hw[4 * dd + s4], acc);
+      const float sc = bf16_lo(sbw[p][s]), bi = bf16_hi(sbw[p][s]);
+      const int bidx = p * NB + sl;
+      y[p] += ldexpf(fmaf(sc, acc, (bi - 128.0f * sc) * lds_hs[bidx]), lds_he[bidx]);
+    }
+  }
+  FUSED_MARK(4);
+  if (r > 0) {  // lambda B_down v
+    for (unsigned n = 0;; ++n) {
+      if (round_done(a, tid >= nv || has_tag(vw, tag), n)) break;
+      vw = ld_dev(&v_c[min(tid, nv - 1)]);
+    }
+    if (tid < nv) lds_v[(tid / r) * kMaxR + tid % r] = wf(vw);
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kFusedMaxP; ++p)
+      if (p < P && sub < r) y[p] = fmaf(a.lam * bf16_to_f32(bdraw[p]), lds_v[p * kMaxR + sub], y[p]);
+  }
+  FUSED_MARK(5);
   float o[kFusedMaxT];
 #pragma unroll
   for (int t = 0; t < kFusedMaxT; ++t) o[t] = 0.f;
 #pragma unroll
   for (int p = 0; p < kFusedMaxP; ++p) {
     if (p >= P) continue;
-    uint32_t hw[16];
-    const uint4* hp = reinterpret_cast<const uint4*>(lds_hh + p * I + 32 * sub);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint4 v = hp[k];
-      hw[4 * k] = v.x; hw[4 * k + 1] = v.y; hw[4 * k + 2] = v.z; hw[4 * k + 3] = v.w;
-    }
-    float y = slice_dot<true>(q[p], sbw[p], hw, lds_hs[p * (I / 32) + sub]);
-    y = ldexpf(y, lds_he[p * (I / 32) + sub]);
-    if (sub < r) y = fmaf(a.lam * bf16_to_f32(bdraw[p]), lds_v[p * kMaxR + sub], y);
-    y = group_sum<G::LPR>(y);
+    const float yp = group_sum<LPR>(y[p]);
     const int t = p / KS;
     const float wk = lds_wt[p];
 #pragma unroll
     for (int tt = 0; tt < kFusedMaxT; ++tt)
-      if (tt == t) o[tt] = fmaf(wk, y, o[tt]);
+      if (tt == t) o[tt] = fmaf(wk, yp, o[tt]);
   }
   if (valid && sub == 0) {
 #pragma unroll
@@ -681,25 +820,32 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
 template <int H, int I>
 __global__ void __launch_bounds__(256) k_fused_decode(FusedArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_hh[kFusedMaxP * I];
-  __shared__ float lds_hs[kFusedMaxP * I / 32];
-  __shared__ int lds_he[kFusedMaxP * I / 32];
-  __shared__ __attribute__((aligned(16))) float lds_f[kFusedMaxP * kMaxR + 160];
+  __shared__ float lds_hs[kFusedMaxP * I / kFusedJW];
+  __shared__ int lds_he[kFusedMaxP * I / kFusedJW];
+  __shared__ __attribute__((aligned(16))) float lds_f[kFusedMaxP * kMaxR + 64];
   __shared__ float lds_wt[kFusedMaxP];
   __shared__ int lds_i[kFusedMaxP];
+  static_assert(4 * (2 * kFusedJW / 4) + 2 * kFusedJW <= kFusedMaxP * kMaxR + 64, "gate/up LDS");
+  static_assert(16 * kMaxR <= kFusedMaxP * I / 2, "v reducer LDS");
+  static_assert(kFusedMaxP <= 8, "one selection slot per lane of an 8-lane group");
   const int b = blockIdx.x;
+  FUSED_MARK(0);
   if (b < a.nR) {
     role_router<H>(a, b);
   } else if (b < a.base_gu) {
     const int i = b - a.base_la;
     role_lora_a<H>(a, i / a.nWA, i % a.nWA, lds_i);
-  } else if (b < a.base_dn) {
+  } else if (b < a.base_v) {
     const int i = b - a.base_gu;
     role_gate_up<H>(a, i / a.nBG, i % a.nBG, lds_f, lds_i);
+  } else if (b < a.base_dn) {
+    role_vred<I>(a, b - a.base_v, reinterpret_cast<float*>(lds_hh));
   } else {
     role_down<H, I>(a, b - a.base_dn, lds_hh, lds_hs, lds_he, lds_f, lds_wt, lds_i);
   }
   // the last workgroup out starts the next epoch
   __syncthreads();
+  FUSED_MARK(7);
   if (threadIdx.x == 0 && add_dev(slot(a, kSlotDone), 1) == a.total - 1) {
     const int e = ld_dev(slot(a, kSlotEpoch));
     if (a.err_out) {  // every other workgroup has finished: the word is final
@@ -719,10 +865,12 @@ static hipError_t launch_fused_t(FusedArgs a, hipStream_t st) {
   a.nR = (a.E + a.S + 4 * RPL_H - 1) / (4 * RPL_H);
   a.nWA = a.r > 0 ? (2 * a.r + 4 * RPL_H - 1) / (4 * RPL_H) : 0;
   a.nBG = a.I / kFusedJW;
-  a.nD = (H + 4 * Geo<I>::RPL - 1) / (4 * Geo<I>::RPL);
+  a.nV = a.r > 0 ? 1 : 0;
+  a.nD = (H + 4 * DGeo<I>::RPL - 1) / (4 * DGeo<I>::RPL);
   a.base_la = a.nR;
   a.base_gu = a.base_la + P * a.nWA;
-  a.base_dn = a.base_gu + P * a.nBG;
+  a.base_v = a.base_gu + P * a.nBG;
+  a.base_dn = a.base_v + P * a.nV;
   a.total = a.base_dn + a.nD;
   hipLaunchKernelGGL((k_fused_decode<H, I>), dim3(a.total), dim3(256), 0, st, a);
   return hipGetLastError();
@@ -736,6 +884,9 @@ bool fused_shape_supported(int H, int I, int r) {
 }
 
 hipError_t launch_fused(const FusedArgs& a, hipStream_t st) {
+  // every workspace region the roles address must be set
+  if (!a.sync || !a.logits || !a.route || !a.wts || !a.u || !a.h || !a.hexp || !a.vpart || !a.v)
+    return hipErrorInvalidValue;
 #define MOE_CASE_I(HV, IV) \
   case IV:                 \
     return launch_fused_t<HV, IV>(a, st);

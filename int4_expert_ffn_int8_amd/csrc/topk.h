@@ -14,52 +14,57 @@ namespace moe {
 
 constexpr uint32_t kNoExpert = 0xFFFFFFFFu;
 
-// (va, ea) ranks before (vb, eb): larger logit, then smaller index
-__device__ __forceinline__ bool topk_before(float va, uint32_t ea, float vb, uint32_t eb) {
-  return va > vb || (va == vb && ea < eb);
-}
-
-// For MP <= 4 logits per lane: each lane sorts its own entries once; a round
-// is then one wave max over the lanes' heads, one wave min over the indices
-// that reach it, and a shift in the winning lane.  emit(k, logit, expert) is
-// called with wave-uniform arguments for k = 0 .. K-1.
+// For MP <= 4 logits per lane.  Each entry becomes one unsigned key that
+// orders like its logit (NaN as -infinity; 0, below every logit, marks an
+// empty entry), and each lane sorts its entries once by (key desc, index
+// asc).  A round is then one wave max over the lanes' head keys; the winner
+// is the only lane holding that key (read from a ballot) or, when several
+// lanes tie, the one with the lowest index; the winning lane shifts its list.
+// emit(k, logit, expert) is called with wave-uniform arguments for
+// k = 0 .. K-1.
 template <int MP, typename Emit>
 __device__ __forceinline__ void topk_wave_sorted(const float* vin, int E, int K, int lane, Emit&& emit) {
   static_assert(MP >= 1 && MP <= 4, "sorted top-K holds at most 4 logits per lane");
-  float v[MP];
+  uint32_t key[MP];
   uint32_t e[MP];
 #pragma unroll
   for (int m = 0; m < MP; ++m) {
     const uint32_t idx = uint32_t(lane + 64 * m);
     const bool ok = idx < uint32_t(E);
-    v[m] = (ok && !isnan(vin[m])) ? vin[m] : -INFINITY;
+    // NaN ranks as -infinity; -0 and +0 are one value (a tie, as compared)
+    const float x = isnan(vin[m]) ? -INFINITY : (vin[m] == 0.f ? 0.f : vin[m]);
+    key[m] = ok ? f32_order_key(x) : 0u;
     e[m] = ok ? idx : kNoExpert;
   }
+  // lane-local insertion sort; entries of a lane have ascending indices, so a
+  // strict key comparison keeps equal keys in index order
 #pragma unroll
   for (int i = 1; i < MP; ++i)
 #pragma unroll
     for (int j = i; j > 0; --j) {
-      const bool sw = topk_before(v[j], e[j], v[j - 1], e[j - 1]);
-      const float tv = v[j];
-      const uint32_t te = e[j];
-      v[j] = sw ? v[j - 1] : v[j];
+      const bool sw = key[j] > key[j - 1];
+      const uint32_t tk = key[j], te = e[j];
+      key[j] = sw ? key[j - 1] : key[j];
       e[j] = sw ? e[j - 1] : e[j];
-      v[j - 1] = sw ? tv : v[j - 1];
+      key[j - 1] = sw ? tk : key[j - 1];
       e[j - 1] = sw ? te : e[j - 1];
     }
   for (int k = 0; k < K; ++k) {
-    const float mx = wave_max(v[0]);
-    const uint32_t sel = wave_min_u32(v[0] == mx ? e[0] : kNoExpert);
+    const uint32_t kmax = wave_max_u32(key[0]);
+    const unsigned long long m = __ballot(key[0] == kmax);
+    const uint32_t sel = ((m & (m - 1)) == 0)  // one lane holds it (m != 0)
+                             ? uint32_t(__builtin_amdgcn_readlane(int(e[0]), __builtin_ctzll(m)))
+                             : wave_min_u32(key[0] == kmax ? e[0] : kNoExpert);
     if (e[0] == sel) {
 #pragma unroll
-      for (int m = 0; m + 1 < MP; ++m) {
-        v[m] = v[m + 1];
-        e[m] = e[m + 1];
+      for (int j = 0; j + 1 < MP; ++j) {
+        key[j] = key[j + 1];
+        e[j] = e[j + 1];
       }
-      v[MP - 1] = -INFINITY;
+      key[MP - 1] = 0u;
       e[MP - 1] = kNoExpert;
     }
-    emit(k, mx, sel);
+    emit(k, f32_from_order_key(kmax), sel);
   }
 }
 

@@ -232,3 +232,20 @@ def test_block_decode_noalloc_validates_before_device_work(B):
     assert lib.moe_block_decode_noalloc(*args(1, flags=8)) == 1
     assert lib.moe_block_decode_noalloc(*args(1, dd=B.dims(2048, 512, 256, 4, 17, 1))) == 2
     assert b"noalloc" in lib.moe_last_error()
+
+
+def test_noalloc_scratch_holds_every_supported_fused_shape(B):
+    # the allocation-free decode's scratch (MOE_NOALLOC_SCRATCH_BYTES) holds
+    # the fused workspace of the largest supported shapes: 8 (token, slot)
+    # pairs, I = 2048, r = 16, and 4 tokens over 1024 experts
+    import re
+    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
+    cap = int(re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES (\d+)", hdr).group(1))
+    worst = 0
+    for T, K, S in [(4, 1, 1), (1, 8, 0), (2, 3, 1), (1, 7, 1), (4, 2, 0)]:
+        for E in (K, 256, 1024):
+            d = B.dims(2048, 2048, E, K, 16, S)
+            n = int(B.load().moe_block_decode_workspace_bytes(B.ctypes.byref(d), T))
+            assert n > 0
+            worst = max(worst, n)
+    assert worst <= cap, (worst, cap)
