@@ -10,7 +10,8 @@
 // Per (token, slot) pair p -- slot k < K is the k-th routed expert, slot K
 // the shared expert -- three kernels run:
 //   k_lora_a_decode   resolve the expert's blob through the pool table, and
-//                     u = [A_gate; A_up] x  (2r dot products over H)
+//                     u = [A_gate; A_up] x  (2r dot products over H, a few
+//                     rows per workgroup)
 //   k_gateup_decode   a_g, a_u rows (+ lambda B u), h = silu(a_g) * a_u (fp16),
 //                     and per-workgroup partials of v = A_down h
 //   k_down_decode     y = deq(Q_down) h + lambda B_down v
@@ -102,48 +103,48 @@ __device__ __forceinline__ float int4_slice_dot(const uint4 q, uint32_t sbw, con
 }
 
 // ---------------------------------------------------------------------------
-// u = [A_gate; A_up] x for one pair; also resolves and records the blob.
-// grid NP, block 256.
+// u = [A_gate; A_up] x, RPL rows per wave and 4 RPL rows per workgroup;
+// workgroup (p, 0) also records the pair's blob (and counts the pool lookup).
+// grid (NP, lora_a_blocks), block 256.
+template <int H>
+constexpr int lora_a_rows_per_block() { return 4 * Geo<H>::RPL; }
+
 template <int H>
 __global__ void __launch_bounds__(256) k_lora_a_decode(DecodeArgs a) {
   using G = Geo<H>;
-  __shared__ const uint8_t* blob_s;
   const int p = blockIdx.x;
-  if (threadIdx.x == 0) {
-    blob_s = resolve_blob(a, p, true);
-    a.blobptr[p] = reinterpret_cast<unsigned long long>(blob_s);
-  }
-  __syncthreads();
+  const uint8_t* blob = resolve_blob(a, p, blockIdx.y == 0);
+  if (blockIdx.y == 0 && threadIdx.x == 0)
+    a.blobptr[p] = reinterpret_cast<unsigned long long>(blob);
   if (a.r == 0) return;
-  const uint8_t* blob = blob_s;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane % G::LPR;
   const int t = p / (a.K + a.S);
+  const int rows = 2 * a.r;
+  const int row = (blockIdx.y * 4 + wave) * G::RPL + lane / G::LPR;
+  const uint16_t* A = reinterpret_cast<const uint16_t*>(blob + a.L.a_gu);
+  // the row's loads first (clamped to a valid row), then the token
+  const int rc = min(row, rows - 1);
+  uint4 q[G::SL][4];
+#pragma unroll
+  for (int c = 0; c < G::SL; ++c)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      q[c][k] = reinterpret_cast<const uint4*>(A + size_t(rc) * H + 32 * sub + 2048 * c)[k];
   uint32_t xw[G::SL][16];
   float xs[G::SL];
   load_vec_slices<H>(a.x + size_t(t) * H, sub, xw, xs);
-  const uint16_t* A = reinterpret_cast<const uint16_t*>(blob + a.L.a_gu);
-  const int rows = 2 * a.r;
-  const int nsets = (rows + G::RPL - 1) / G::RPL;
-  for (int rs = wave; rs < nsets; rs += 4) {
-    const int row = rs * G::RPL + lane / G::LPR;
-    float acc = 0.f;
-    if (row < rows) {
+  float acc = 0.f;
 #pragma unroll
-      for (int c = 0; c < G::SL; ++c) {
-        const uint4* ap = reinterpret_cast<const uint4*>(A + size_t(row) * H + 32 * sub + 2048 * c);
+  for (int c = 0; c < G::SL; ++c)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint4 q = ap[k];
-          acc = dot2_bf16(q.x, xw[c][4 * k], acc);
-          acc = dot2_bf16(q.y, xw[c][4 * k + 1], acc);
-          acc = dot2_bf16(q.z, xw[c][4 * k + 2], acc);
-          acc = dot2_bf16(q.w, xw[c][4 * k + 3], acc);
-        }
-      }
+    for (int k = 0; k < 4; ++k) {
+      acc = dot2_bf16(q[c][k].x, xw[c][4 * k], acc);
+      acc = dot2_bf16(q[c][k].y, xw[c][4 * k + 1], acc);
+      acc = dot2_bf16(q[c][k].z, xw[c][4 * k + 2], acc);
+      acc = dot2_bf16(q[c][k].w, xw[c][4 * k + 3], acc);
     }
-    acc = group_sum<G::LPR>(acc);
-    if (row < rows && sub == 0) a.u[size_t(p) * rows + row] = acc;
-  }
+  acc = group_sum<G::LPR>(acc);
+  if (row < rows && sub == 0) a.u[size_t(p) * rows + row] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -227,6 +228,7 @@ __global__ void __launch_bounds__(256) k_down_decode(DecodeArgs a, int NB) {
   using G = Geo<I>;
   using D = DownGeo<I>;
   __shared__ float vs[kMaxR];
+  __shared__ float vg[16][kMaxR];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = lane % G::LPR;
   const int p = blockIdx.x;
   const int H = a.H, r = a.r;
@@ -251,11 +253,22 @@ __global__ void __launch_bounds__(256) k_down_decode(DecodeArgs a, int NB) {
       }
     }
   }
-  if (threadIdx.x < r) {
-    const float* vp = a.vpart + size_t(p) * NB * r + threadIdx.x;
+  // v = sum of the NB <= I / 8 partials: thread (rank tid % 16, group tid / 16)
+  // adds blocks group, group + 16, ... (all its loads issued at once), and the
+  // 16 group sums of a rank are added in group order below.
+  constexpr int NBG = (I / 8 + 15) / 16;
+  static_assert(kMaxR == 16, "one rank per lane of a 16-lane group");
+  if (r > 0) {
+    const int rr = threadIdx.x & 15, bg = threadIdx.x >> 4;
+    const float* vp = a.vpart + size_t(p) * NB * r + min(rr, r - 1);
+    float w[NBG];
+#pragma unroll
+    for (int k = 0; k < NBG; ++k) w[k] = vp[size_t(min(bg + 16 * k, NB - 1)) * r];
     float s = 0.f;
-    for (int b = 0; b < NB; ++b) s += vp[size_t(b) * r];
-    vs[threadIdx.x] = s;
+#pragma unroll
+    for (int k = 0; k < NBG; ++k)
+      if (bg + 16 * k < NB) s += w[k];
+    vg[bg][rr] = s;
   }
   // h slices as fp16(h * 2^-e), one exponent per 32-column slice
   uint32_t xw[G::SL][16];
@@ -282,6 +295,13 @@ __global__ void __launch_bounds__(256) k_down_decode(DecodeArgs a, int NB) {
       sum += float(pr[0]) + float(pr[1]);
     }
     xs[c] = sum;
+  }
+  __syncthreads();
+  if (threadIdx.x < r) {
+    float v = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) v += vg[g][threadIdx.x];
+    vs[threadIdx.x] = v;
   }
   __syncthreads();
   const uint16_t* Bd = reinterpret_cast<const uint16_t*>(blob + a.L.b_dn);
@@ -318,7 +338,9 @@ int decode_gateup_block_j(int H) {
 
 template <int H>
 static hipError_t launch_front(const DecodeArgs& a, int NP, hipStream_t st) {
-  hipLaunchKernelGGL(k_lora_a_decode<H>, dim3(NP), dim3(256), 0, st, a);
+  const int ra = lora_a_rows_per_block<H>();
+  const int ny = a.r > 0 ? (2 * a.r + ra - 1) / ra : 1;
+  hipLaunchKernelGGL(k_lora_a_decode<H>, dim3(NP, ny), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_gateup_decode<H>, dim3(NP, a.I / GateUpGeo<H>::JW), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -346,6 +368,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
 #undef MOE_CASE
   if (e != hipSuccess) return e;
   const int NB = a.I / decode_gateup_block_j(a.H);
+  if (NB < 1 || 8 * NB > a.I) return hipErrorInvalidValue;  // k_down_decode sums <= I / 8 partials
 #define MOE_CASE(V)                      \
   case V:                                \
     return launch_back<V>(a, NP, NB, st);
