@@ -313,9 +313,16 @@ MOE_API moe_status_t moe_block_decode_noalloc(const moe_dims_t* d, const int8_t*
  *   z = W2 silu(W1 h), pred = top-K of z ordered by (-z, index).
  *   W1 device bf16 [D, H], W2 bf16 [E, D], h bf16 [T, H];
  *   pred_idx int32 [T, K]; pred_logits fp32 [T, E] or NULL.
- *   ws: at least prerouter_workspace_bytes(D, E, T) bytes.
+ *   One kernel launch per call: workgroups of W1 rows hand partial logits to
+ *   one workgroup per token, which adds them in a fixed order and selects.
+ *   ws: device, at least prerouter_workspace_bytes(D, E, T) bytes, ZEROED
+ *   ONCE before its first use (it holds the launch epoch and an arrival
+ *   counter); later calls find it as the previous call left it.  Calls that
+ *   share a workspace must not overlap (issue them on one stream).  Should a
+ *   bounded in-kernel wait run out (a launch that cannot make progress), the
+ *   token's pred_idx entries are -1.
  *   Supported: H as above, D a multiple of 64 up to 4096, 1 <= K <= 16,
- *   K <= E <= 1024. */
+ *   K <= E <= 1024, T <= 65535. */
 MOE_API size_t prerouter_workspace_bytes(int32_t D, int32_t E, int32_t T);
 MOE_API moe_status_t prerouter_predict(const uint16_t* W1, const uint16_t* W2, int32_t H, int32_t D,
                                int32_t E, int32_t K, const uint16_t* h, int32_t T,
@@ -328,8 +335,10 @@ MOE_API moe_status_t prerouter_predict(const uint16_t* W1, const uint16_t* W2, i
  * input is h with the one-hot of the experts the layer executed appended,
  *   z = W2 silu(W1 [h; onehot(prev)]), pred = top-K of z ordered by (-z, index).
  *   W1 device bf16 [D, H + E] (columns H + e weight expert e); prev_idx
- *   device int32 [T, Kp] (ids outside [0, E) are ignored, so -1 pads);
- *   everything else as prerouter_predict.  Supported: 0 <= Kp <= 16. */
+ *   device int32 [T, Kp] (ids outside [0, E) are ignored, so -1 pads; a
+ *   repeated id counts once: the one-hot is an indicator vector);
+ *   everything else as prerouter_predict.  Supported: 0 <= Kp <= 16, and
+ *   H + E a multiple of 8 (16-byte W1 rows), else MOE_EUNSUPPORTED. */
 MOE_API moe_status_t prerouter_predict_feat(const uint16_t* W1, const uint16_t* W2, int32_t H,
                                             int32_t D, int32_t E, int32_t K, const uint16_t* h,
                                             const int32_t* prev_idx, int32_t Kp, int32_t T,

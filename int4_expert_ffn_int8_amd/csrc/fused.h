@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/moe.h"
+#include "handoff.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -28,8 +29,6 @@ constexpr size_t kSyncBytes = size_t(kNumSlots) * kSlotInts * 4;
 static_assert(kSyncBytes == MOE_DECODE_SYNC_BYTES, "header constant");
 static_assert(kSlotErr * kSlotInts * 4 == MOE_DECODE_ERR_OFFSET, "header constant");
 
-// A hand-off word: tag in the high 32 bits, payload bits in the low 32.
-typedef unsigned long long tword_t;
 
 struct FusedArgs {
   int T, E, K, S, r, H, I, norm_topk;

@@ -55,6 +55,7 @@
 // run in a second pass.
 #include "device_utils.h"
 #include "fused.h"
+#include "handoff.h"
 #include "launch.h"
 #include "moe_internal.h"
 #include "topk.h"
@@ -67,29 +68,12 @@
 
 namespace moe {
 
-template <typename T>
-__device__ __forceinline__ T ld_dev(const T* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ void st_dev(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int add_dev(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ int* slot(const FusedArgs& a, int s) { return a.sync + s * kSlotInts; }
 
 // this launch's tag (epoch + 1, never 0)
 __device__ __forceinline__ unsigned launch_tag(const FusedArgs& a) {
-  return (unsigned(ld_dev(slot(a, kSlotEpoch))) % 0x7FFFFFFFu) + 1u;
+  return epoch_tag(slot(a, kSlotEpoch));
 }
-__device__ __forceinline__ tword_t tw(unsigned tag, uint32_t bits) {
-  return (tword_t(tag) << 32) | bits;
-}
-__device__ __forceinline__ tword_t twf(unsigned tag, float v) { return tw(tag, __float_as_uint(v)); }
-__device__ __forceinline__ bool has_tag(tword_t w, unsigned tag) { return unsigned(w >> 32) == tag; }
-__device__ __forceinline__ float wf(tword_t w) { return __uint_as_float(uint32_t(w)); }
 
 // the copy of broadcast words this workgroup reads: its XCD's (workgroups
 // are spread over the 8 XCDs round-robin by id)
@@ -844,16 +828,11 @@ __global__ void __launch_bounds__(256) k_fused_decode(FusedArgs a) {
     role_down<H, I>(a, b - a.base_dn, lds_hh, lds_hs, lds_he, lds_f, lds_wt, lds_i);
   }
   // the last workgroup out starts the next epoch
-  __syncthreads();
   FUSED_MARK(7);
-  if (threadIdx.x == 0 && add_dev(slot(a, kSlotDone), 1) == a.total - 1) {
-    const int e = ld_dev(slot(a, kSlotEpoch));
-    if (a.err_out) {  // every other workgroup has finished: the word is final
-      *a.err_out = ld_dev(slot(a, kSlotErr));
-      st_dev(slot(a, kSlotErr), 0);
-    }
-    st_dev(slot(a, kSlotDone), 0);
-    st_dev(slot(a, kSlotEpoch), e + 1);
+  if (finish_launch(slot(a, kSlotEpoch), slot(a, kSlotDone), a.total) && a.err_out) {
+    // every other workgroup has finished: the error word is final
+    *a.err_out = ld_dev(slot(a, kSlotErr));
+    st_dev(slot(a, kSlotErr), 0);
   }
 }
 

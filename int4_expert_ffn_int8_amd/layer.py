@@ -181,7 +181,8 @@ class MoeStack:
 
     def __init__(self, H, I, E, K, r, n_shared, lora_scale, routers, shared_blobs, routed=None,
                  host_blobs=None, pool_slots=0, prerouter=None, pred_k=0, eps=1e-6,
-                 max_fills=-1, exec_mode="router", prerouter_feat=False, device="cuda"):
+                 max_fills=-1, exec_mode="router", prerouter_feat=False, overlap_heads=True,
+                 device="cuda"):
         self.H, self.I, self.E, self.K, self.r, self.S = H, I, E, K, r, n_shared
         self.L = len(routers)
         self.d = B.dims(H, I, E, K, r, n_shared, lora_scale, 1)
@@ -209,6 +210,14 @@ class MoeStack:
         self.prerouter = prerouter
         self.prerouter_feat = prerouter_feat
         self.pred_k = pred_k
+        # Prerouter heads run on a stream of their own, each after its layer's
+        # kernel, so a head overlaps the next layer instead of delaying it
+        # (default priority, like every stream here)
+        self.overlap_heads = overlap_heads and prerouter is not None
+        if self.overlap_heads:
+            self.head_stream = torch.cuda.Stream(device=dv)
+            self.ev_out = [torch.cuda.Event() for _ in range(self.L)]
+            self.ev_head = [torch.cuda.Event() for _ in range(self.L)]
         self.exec_mode = "router"
         self.have_pred = False
         T = 1
@@ -220,7 +229,8 @@ class MoeStack:
         self.h = [torch.empty((T, H), dtype=torch.int16, device=dv) for _ in range(2)]
         if prerouter is not None:
             D = prerouter[0][0].shape[0]
-            self.pr_ws = torch.empty((B.prerouter_workspace_bytes(D, E, T),), dtype=torch.uint8,
+            # zeroed once: the head's launch epoch and arrival counter live there
+            self.pr_ws = torch.zeros((B.prerouter_workspace_bytes(D, E, T),), dtype=torch.uint8,
                                      device=dv)
             self.pred = torch.full((self.L, T, pred_k), -1, dtype=torch.int32, device=dv)
             self.pred_exec = torch.full((self.L, T, pred_k), -1, dtype=torch.int32, device=dv)
@@ -262,26 +272,46 @@ class MoeStack:
         else:
             B.moe_block_decode(*args, self.idx[l], self.w[l], out, self.ws, stream)
 
+    @staticmethod
+    def _torch_stream(stream):
+        if stream is None:
+            return torch.cuda.current_stream()
+        if isinstance(stream, int):
+            return torch.cuda.ExternalStream(stream) if stream else torch.cuda.default_stream()
+        return stream
+
     def step(self, x, stream=None, outs=None):
         """One token through every layer; returns the output hidden state.
-        outs: optional per-layer output buffers (default: two alternating)."""
+        outs: optional per-layer output buffers (default: two alternating).
+        Every kernel of the step, heads included, is ordered before work issued
+        later on `stream`."""
+        s = self._torch_stream(stream)
+        hs = self.head_stream if self.overlap_heads else s
         cur = x
         for l in range(self.L):
             out = self.h[l % 2] if outs is None else outs[l]
-            self.layer_forward(l, cur, out, stream)
+            if self.overlap_heads and outs is None and l >= 2:
+                s.wait_event(self.ev_head[l - 2])  # head l-2 has read this buffer
+            self.layer_forward(l, cur, out, s)
             if self.prerouter is not None and l + 1 < self.L:
+                if self.overlap_heads:
+                    self.ev_out[l].record(s)
+                    hs.wait_event(self.ev_out[l])
                 W1, W2 = self.prerouter[l]
                 if self.prerouter_feat:  # h plus the one-hot of this layer's executed experts
                     B.prerouter_predict_feat(W1, W2, self.H, W1.shape[0], self.E, self.pred_k, out,
                                              self.idx[l], self.K, 1, self.pred[l + 1], None,
-                                             self.pr_ws, stream)
+                                             self.pr_ws, hs)
                 else:
                     B.prerouter_predict(W1, W2, self.H, W1.shape[0], self.E, self.pred_k, out, 1,
-                                        self.pred[l + 1], None, self.pr_ws, stream)
+                                        self.pred[l + 1], None, self.pr_ws, hs)
+                if self.overlap_heads:
+                    self.ev_head[l].record(hs)
             cur = out
+        if self.overlap_heads:
+            s.wait_stream(hs)
         if self.exec_mode == "predict":
             # this step's predictions are the next step's routes
-            s = torch.cuda.current_stream() if stream is None else stream
             with torch.cuda.stream(s):
                 self.pred_exec.copy_(self.pred)
             self.have_pred = True

@@ -128,6 +128,15 @@ def test_prerouter_validation(B):
                                       1 << 20, 0) == 1
     assert B.load().prerouter_predict(fake, fake, 2048, 256, 256, 4, fake, 1, fake, None, fake,
                                       16, 0) == 4
+    # features: W1 rows of H + E columns must be 16-byte multiples
+    assert B.load().prerouter_predict_feat(fake, fake, 2048, 256, 100, 4, fake, fake, 4, 1, fake,
+                                           None, fake, 1 << 20, 0) == 2
+    assert B.load().prerouter_predict(fake, fake, 2048, 256, 256, 4, fake, 1 << 16, fake, None,
+                                      fake, 1 << 40, 0) == 2
+    # the workspace holds the launch counter and the partial logits of ceil(D / 8)
+    # row blocks per token, as 8-byte hand-off words
+    assert B.prerouter_workspace_bytes(256, 256, 1) >= 256 + 32 * 256 * 8
+    assert B.prerouter_workspace_bytes(4096, 1000, 3) >= 256 + 3 * 512 * 1000 * 8
 
 
 def _unpack_codes(rows_bytes, n):

@@ -114,3 +114,32 @@ def test_pool_results_do_not_depend_on_residency():
         np.testing.assert_array_equal(pooled.table[l].cpu().numpy(), pooled.pool.table(l))
     for st in (resident, pooled, never):
         assert st.error_word() == 0
+
+
+@pytest.mark.parametrize("mode,feat", [("router", False), ("predict", False), ("predict", True)])
+def test_heads_on_their_own_stream_match_serial_heads(mode, feat):
+    # Prerouter heads overlapped with the next layers (own stream, the layer
+    # buffers reused two layers on) give the same outputs, routes and
+    # predictions, bit for bit, as heads issued between the layers
+    from int4_expert_ffn_int8_amd.layer import dev
+    w = synth.workload(0, prerouter_D=64)
+    nl, pred_k, steps = 5, w["K"], 4
+    routers, _, _, blobs, shared_dev = _stack_weights(w, nl)
+    gen = synth.prerouter_feat_tensors if feat else synth.prerouter_tensors
+    heads = [(dev(p["W1"]), dev(p["W2"])) for p in (gen(w, l) for l in range(nl - 1))]
+    stacks = [_pool_stack(w, routers, shared_dev, blobs, heads, pred_k, routed=dev(blobs),
+                          exec_mode=mode, prerouter_feat=feat, overlap_heads=ov)
+              for ov in (True, False)]
+    assert stacks[0].overlap_heads and not stacks[1].overlap_heads
+    for step in range(steps):
+        x = dev(synth.tokens(w, 300 + step))
+        got = []
+        for st in stacks:
+            o = st.step(x)
+            torch.cuda.synchronize()
+            got.append((_bits(o).copy(), st.idx.cpu().numpy().copy(), st.pred.cpu().numpy().copy()))
+        for a, b in zip(got[0], got[1]):
+            np.testing.assert_array_equal(a, b, err_msg=f"{mode} feat={feat} step {step}")
+        assert (got[0][2][1:] >= 0).all()  # every head predicted
+    for st in stacks:
+        assert st.error_word() == 0

@@ -510,11 +510,16 @@ def test_prerouter_feat_pins():
         zb = [math.fsum(bfv(W2[e][d]) * a[d] for d in range(D)) for e in range(E)]
         assert np.allclose(z[t], zb, rtol=1e-12, atol=1e-15)
         assert pred[t].tolist() == sorted(range(E), key=lambda e: (-zb[e], e))[:K]
-    # (3) order and padding of the executed list do not matter
+    # (3) order, padding and repeats of the executed list do not matter (the
+    # one-hot is an indicator: an expert executed is 1 however often listed)
     prev2 = np.array([[7, 1, 4, -1], [9, -5, 0, 12]], np.int32)
     p2, z2 = O.prerouter_feat(W1, W2, h, prev2, K)
     np.testing.assert_array_equal(p2, pred)
     np.testing.assert_allclose(z2, z, rtol=1e-13, atol=1e-15)
+    prev3 = np.array([[4, 4, 1, 7, 1, 4], [0, 0, 9, 9, 9, -1]], np.int32)
+    p3, z3 = O.prerouter_feat(W1, W2, h, prev3, K)
+    np.testing.assert_array_equal(p3, pred)
+    np.testing.assert_allclose(z3, z, rtol=1e-13, atol=1e-15)
     # (4) a large weight on one feature column into a hidden unit that feeds
     # only expert 5 makes expert 5 the first prediction for tokens that
     # executed expert 2, and changes nothing for tokens that did not
