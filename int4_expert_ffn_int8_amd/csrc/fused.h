@@ -16,10 +16,10 @@ constexpr int kFusedJW = 16;     // gate/up outputs per workgroup = columns per 
 constexpr int kCopies = 8;       // copies of each broadcast hand-off word (one per XCD)
 constexpr unsigned kFusedSpinLimit = 1u << 20;  // bounded waits (~0.2 s)
 
-// Control words at the start of the fused workspace, one 256-byte slot each.
-// The launch epoch is bumped by the last workgroup of every launch; all
-// hand-off data is tagged with (epoch + 1), so words left by earlier launches
-// never look valid and nothing needs clearing between launches.
+// Control words at the start of the fused workspace, one 256-byte slot each:
+// the 64-bit launch counter that tags all hand-off data (words left by earlier
+// launches never look valid, so nothing needs clearing between launches), the
+// arrival count of launches that report their error word, the error word.
 constexpr int kSlotInts = 64;
 constexpr int kSlotEpoch = 0;
 constexpr int kSlotDone = 1;

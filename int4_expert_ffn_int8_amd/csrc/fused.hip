@@ -70,9 +70,13 @@ namespace moe {
 
 __device__ __forceinline__ int* slot(const FusedArgs& a, int s) { return a.sync + s * kSlotInts; }
 
-// this launch's tag (epoch + 1, never 0)
+__device__ __forceinline__ unsigned long long* launch_counter(const FusedArgs& a) {
+  return reinterpret_cast<unsigned long long*>(slot(a, kSlotEpoch));
+}
+// this launch's tag (never 0); every thread may read it until its workgroup
+// arrives at the kernel's end
 __device__ __forceinline__ unsigned launch_tag(const FusedArgs& a) {
-  return epoch_tag(slot(a, kSlotEpoch));
+  return counter_tag(counter_read(launch_counter(a)));
 }
 
 // the copy of broadcast words this workgroup reads: its XCD's (workgroups
@@ -827,9 +831,12 @@ __global__ void __launch_bounds__(256) k_fused_decode(FusedArgs a) {
   } else {
     role_down<H, I>(a, b - a.base_dn, lds_hh, lds_hs, lds_he, lds_f, lds_wt, lds_i);
   }
-  // the last workgroup out starts the next epoch
+  // the workgroup's share of the launch counter (every read of it is done);
+  // with err_out, the last workgroup out also moves the error word there
   FUSED_MARK(7);
-  if (finish_launch(slot(a, kSlotEpoch), slot(a, kSlotDone), a.total) && a.err_out) {
+  __syncthreads();
+  if (threadIdx.x == 0) counter_arrive(launch_counter(a), 0, b, a.total);
+  if (a.err_out && last_to_arrive(slot(a, kSlotDone), a.total)) {
     // every other workgroup has finished: the error word is final
     *a.err_out = ld_dev(slot(a, kSlotErr));
     st_dev(slot(a, kSlotErr), 0);

@@ -7,9 +7,9 @@
 // and read with device-scope relaxed atomics, which are served at the memory
 // side and bypass the XCD L2s.  A producer just stores; a consumer loads the
 // words it needs and repeats the loads until all of them carry this launch's
-// tag.  The tag is a per-workspace launch epoch + 1 that the last workgroup of
-// every launch bumps, so words left by earlier launches never look valid and
-// nothing needs clearing between launches.
+// tag.  The tag comes from a per-workspace launch counter (below) that grows
+// by a fixed amount per launch, so words left by earlier launches never look
+// valid and nothing needs clearing between launches.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,10 +32,6 @@ __device__ __forceinline__ int add_dev(int* p, int v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// the tag of the launch that reads epoch word *ep (epoch + 1, never 0)
-__device__ __forceinline__ unsigned epoch_tag(const int* ep) {
-  return (unsigned(ld_dev(ep)) % 0x7FFFFFFFu) + 1u;
-}
 __device__ __forceinline__ tword_t tw(unsigned tag, uint32_t bits) {
   return (tword_t(tag) << 32) | bits;
 }
@@ -44,21 +40,22 @@ __device__ __forceinline__ bool has_tag(tword_t w, unsigned tag) { return unsign
 __device__ __forceinline__ float wf(tword_t w) { return __uint_as_float(uint32_t(w)); }
 
 // Launch counter without a returning atomic.  *ctr (64-bit, zero before the
-// first launch) grows by exactly 2^32 per launch: one thread of each of the
-// launch's `total` workgroups reads it once (counter_read) and then adds the
-// workgroup's share (counter_arrive).  A workgroup reads before its own add,
-// so every read of a launch returns a value in [n 2^32, (n + 1) 2^32) and the
-// whole launch derives the same tag from n (counter_tag), whatever the order
-// in which its workgroups run; launches of different grid sizes may share the
-// counter.  The adds are fire-and-forget: no workgroup waits for them.  A
-// second read after the add could see the next launch's epoch, so the reading
-// thread hands the tag to the rest of its workgroup (through LDS).
+// first launch) grows by exactly 2^32 per launch: each of the launch's `total`
+// workgroups adds its share once (counter_arrive), after the last read of the
+// counter by any of its threads.  Every read of a launch then returns a value
+// in [n 2^32, (n + 1) 2^32) -- the other workgroups' shares sum to less than
+// 2^32 -- and the whole launch derives the same tag from n (counter_tag),
+// whatever the order in which its workgroups run; launches of different grid
+// sizes may share the counter.  The adds are fire-and-forget: no workgroup
+// waits for them.
 __device__ __forceinline__ unsigned long long counter_read(const unsigned long long* ctr) {
   return ld_dev(ctr);
 }
 __device__ __forceinline__ unsigned counter_tag(unsigned long long c) {
   return unsigned((c >> 32) % 0x7FFFFFFFull) + 1u;
 }
+// `c`: a value this thread read from the counter; the add waits for it, so a
+// workgroup whose only reader is this thread may add right after its read.
 __device__ __forceinline__ void counter_arrive(unsigned long long* ctr, unsigned long long c, int wg,
                                                int total) {
   const unsigned long long q = (1ull << 32) / unsigned(total);
@@ -69,17 +66,14 @@ __device__ __forceinline__ void counter_arrive(unsigned long long* ctr, unsigned
   __hip_atomic_fetch_add(ctr, share, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// End of a workgroup's part of the launch (call after its last hand-off store,
-// from every thread): the last of `total` workgroups to arrive resets the
-// arrival counter *done and starts the next epoch *ep.  Returns true in thread
-// 0 of that last workgroup, whose caller may then act on state every other
-// workgroup has finished with.
-__device__ __forceinline__ bool finish_launch(int* ep, int* done, int total) {
+// Arrival count (call from every thread at the end of a workgroup's part of
+// the launch): true in thread 0 of the last of `total` workgroups to arrive,
+// which also resets *done for the next launch.  A returning atomic: use it
+// only where some workgroup must act after all the others.
+__device__ __forceinline__ bool last_to_arrive(int* done, int total) {
   __syncthreads();
   if (threadIdx.x == 0 && add_dev(done, 1) == total - 1) {
-    const int e = ld_dev(ep);
     st_dev(done, 0);
-    st_dev(ep, e + 1);
     return true;
   }
   return false;

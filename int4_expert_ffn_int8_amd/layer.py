@@ -229,7 +229,7 @@ class MoeStack:
         self.h = [torch.empty((T, H), dtype=torch.int16, device=dv) for _ in range(2)]
         if prerouter is not None:
             D = prerouter[0][0].shape[0]
-            # zeroed once: the head's launch epoch and arrival counter live there
+            # zeroed once: the head's launch counter lives there
             self.pr_ws = torch.zeros((B.prerouter_workspace_bytes(D, E, T),), dtype=torch.uint8,
                                      device=dv)
             self.pred = torch.full((self.L, T, pred_k), -1, dtype=torch.int32, device=dv)
