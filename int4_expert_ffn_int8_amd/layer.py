@@ -181,7 +181,7 @@ class MoeStack:
 
     def __init__(self, H, I, E, K, r, n_shared, lora_scale, routers, shared_blobs, routed=None,
                  host_blobs=None, pool_slots=0, prerouter=None, pred_k=0, eps=1e-6,
-                 max_fills=-1, exec_mode="router", prerouter_feat=False, overlap_heads=True,
+                 max_fills=-1, exec_mode="router", prerouter_feat=False, overlap_heads=False,
                  device="cuda"):
         self.H, self.I, self.E, self.K, self.r, self.S = H, I, E, K, r, n_shared
         self.L = len(routers)
@@ -210,9 +210,11 @@ class MoeStack:
         self.prerouter = prerouter
         self.prerouter_feat = prerouter_feat
         self.pred_k = pred_k
-        # Prerouter heads run on a stream of their own, each after its layer's
-        # kernel, so a head overlaps the next layer instead of delaying it
-        # (default priority, like every stream here)
+        # overlap_heads: each Prerouter head runs on a stream of its own after
+        # its layer's kernel, overlapping the next layer (default priority, like
+        # every stream here).  It costs four event calls per layer on the host,
+        # more than the head's GPU time in an eagerly issued step, so it is for
+        # steps captured in a graph; by default heads run between the layers.
         self.overlap_heads = overlap_heads and prerouter is not None
         if self.overlap_heads:
             self.head_stream = torch.cuda.Stream(device=dv)
