@@ -223,10 +223,15 @@ def moe_rmsnorm(h, T, H, eps, out, stream=None) -> None:
 
 
 def prerouter_workspace_bytes(D: int, E: int, T: int) -> int:
+    """Bytes of the Prerouter's workspace for T tokens. The caller zeroes it
+    once, before the first call, and reuses it: the calls leave its hand-off
+    counter and words in the state the next call expects."""
     return int(load().prerouter_workspace_bytes(D, E, T))
 
 
 def prerouter_predict(W1, W2, H, D, E, K, h, T, pred_idx, pred_logits, ws, stream=None) -> None:
+    """One launch: the head's two layers and its top-K for T tokens. Calls
+    that share a workspace must not overlap (same stream or serialised)."""
     _check(load().prerouter_predict(ptr(W1), ptr(W2), H, D, E, K, ptr(h), T, ptr(pred_idx),
                                     ptr(pred_logits), ptr(ws),
                                     ws.numel() * ws.element_size() if ws is not None else 0,
