@@ -123,7 +123,7 @@ __device__ __forceinline__ float group_sum(float v) {
 // +infinity, so callers map NaN first where that matters).
 __device__ __forceinline__ uint32_t f32_order_key(float f) {
   const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float f32_from_order_key(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);

@@ -240,13 +240,17 @@ __device__ void route_token(const FusedArgs& a, int t, int lane, unsigned tag) {
   float first = 0.f, mine_l = -INFINITY;
   int mine_e = 0;
   if (a.exec_idx == nullptr) {
-    topk_wave(v, a.E, a.K, lane, [&](int k, float mx, uint32_t sel) {
+    auto emit = [&](int k, float mx, uint32_t sel) {
       if (k == 0) first = mx;  // the largest logit
       if (k == kk) {
         mine_l = mx;
         mine_e = int(sel);
       }
-    });
+    };
+    if constexpr (MP > 4)  // E > 256
+      topk_wave_scan<MP>(v, a.E, a.K, lane, emit);
+    else
+      topk_wave(v, a.E, a.K, lane, emit);
   } else {
     // given experts: slot k takes expert exec_idx[t][k] and fetches its logit
     // from the lane that holds it
@@ -267,6 +271,9 @@ __device__ void route_token(const FusedArgs& a, int t, int lane, unsigned tag) {
     mine_l = kk < a.K ? gl : -INFINITY;
     first = wave_max(mine_l);
   }
+  // the ids first: the expert roles wait on them, the weights only the combine
+  const int c = lane >> 3;
+  if (kk < a.K) st_dev(&a.route[(c * a.T + t) * a.K + kk], tw(tag, uint32_t(mine_e)));
   float mine = kk < a.K ? expf(mine_l - first) : 0.f;
   float denom;
   if (a.norm_topk) {
@@ -289,11 +296,7 @@ __device__ void route_token(const FusedArgs& a, int t, int lane, unsigned tag) {
     if (a.user_idx) a.user_idx[t * a.K + lane] = mine_e;
     if (a.user_w) a.user_w[t * a.K + lane] = wv;
   }
-  const int c = lane >> 3;
-  if (kk < a.K) {
-    st_dev(&a.route[(c * a.T + t) * a.K + kk], tw(tag, uint32_t(mine_e)));
-    st_dev(&a.wts[(c * a.T + t) * (a.K + 1) + kk], twf(tag, wv));
-  }
+  if (kk < a.K) st_dev(&a.wts[(c * a.T + t) * (a.K + 1) + kk], twf(tag, wv));
   if (a.S && kk == 0) st_dev(&a.wts[(c * a.T + t) * (a.K + 1) + a.K], twf(tag, sigmoid_f(sgl)));
   if (t == 0) FUSED_MARK(3);
 }
@@ -403,6 +406,10 @@ __device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, 
   const int j0 = blk * JW + wave * JPW;
   const int r = a.r;
   const unsigned tag = launch_tag(a);
+  // the token's input (and its norm) while the route is not yet known
+  uint32_t xw[16];
+  float xs;
+  token_slice<H>(a, t, sub, xw, xs);
   const uint8_t* blob = a.shared_blob;
   if (routed) blob = expert_blob(a, wait_expert(a, p, tag, lds_int), false);
   FUSED_MARK(1);
@@ -430,9 +437,6 @@ __device__ void role_gate_up(const FusedArgs& a, int unit, int blk, float* lds, 
     for (int i = 0; i < NL; ++i) braw[i] = Bgu[size_t(brow[i]) * r + min(sub, rc)];
     adraw = Ad[size_t(min(tid / JW, rc)) * a.I + blk * JW + tid % JW];
   }
-  uint32_t xw[16];
-  float xs;
-  token_slice<H>(a, t, sub, xw, xs);
   float part[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) part[i] = slice_dot_bf16(q[i], sbw[i], xw, xs);

@@ -27,13 +27,16 @@ __device__ __forceinline__ void topk_wave_sorted(const float* vin, int E, int K,
   static_assert(MP >= 1 && MP <= 4, "sorted top-K holds at most 4 logits per lane");
   uint32_t key[MP];
   uint32_t e[MP];
+  constexpr uint32_t kNegInfKey = 0x007FFFFFu;  // f32_order_key(-infinity)
 #pragma unroll
   for (int m = 0; m < MP; ++m) {
     const uint32_t idx = uint32_t(lane + 64 * m);
     const bool ok = idx < uint32_t(E);
-    // NaN ranks as -infinity; -0 and +0 are one value (a tie, as compared)
-    const float x = isnan(vin[m]) ? -INFINITY : (vin[m] == 0.f ? 0.f : vin[m]);
-    key[m] = ok ? f32_order_key(x) : 0u;
+    // -0 + 0 is +0, so -0 and +0 give one key (a tie, as compared); a NaN
+    // stays a NaN and ranks as -infinity (selects, no branches)
+    const float x = vin[m] + 0.0f;
+    const uint32_t kx = f32_order_key(x);
+    key[m] = ok ? (x != x ? kNegInfKey : kx) : 0u;
     e[m] = ok ? idx : kNoExpert;
   }
   // lane-local insertion sort; entries of a lane have ascending indices, so a
@@ -93,17 +96,23 @@ __device__ __forceinline__ void topk_wave_scan(const float* vin, int E, int K, i
   }
 }
 
-// Dispatch on E: vin holds MPMAX entries per lane (only ceil(E/64) are read).
+// Dispatch on E: vin holds MPMAX entries per lane (only ceil(E/64) are read;
+// E <= 64 MPMAX).
 template <int MPMAX, typename Emit>
 __device__ __forceinline__ void topk_wave(const float (&vin)[MPMAX], int E, int K, int lane, Emit&& emit) {
+  static_assert(MPMAX >= 4, "room for the sorted lists of E <= 256");
+  if constexpr (MPMAX > 4) {
+    if (E > 256) {
+      topk_wave_scan<MPMAX>(vin, E, K, lane, emit);
+      return;
+    }
+  }
   if (E <= 64)
     topk_wave_sorted<1>(vin, E, K, lane, emit);
   else if (E <= 128)
     topk_wave_sorted<2>(vin, E, K, lane, emit);
-  else if (E <= 256)
-    topk_wave_sorted<4>(vin, E, K, lane, emit);
   else
-    topk_wave_scan<MPMAX>(vin, E, K, lane, emit);
+    topk_wave_sorted<4>(vin, E, K, lane, emit);
 }
 
 }  // namespace moe
