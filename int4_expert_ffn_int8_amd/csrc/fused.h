@@ -15,6 +15,9 @@ constexpr int kFusedMaxP = 8;    // (token, slot) pairs per fused call
 constexpr int kFusedJW = 16;     // gate/up outputs per workgroup = columns per h exponent
 constexpr int kCopies = 8;       // copies of each broadcast hand-off word (one per XCD)
 constexpr unsigned kFusedSpinLimit = 1u << 20;  // bounded waits (~0.2 s)
+// routed gate/up code bytes of a launch (T K I H) from which the down
+// workgroups defer their routed rows
+constexpr uint64_t kDeferDownBytes = uint64_t(1) << 21;
 
 // Control words at the start of the fused workspace, one 256-byte slot each:
 // the 64-bit launch counter that tags all hand-off data (words left by earlier
@@ -61,6 +64,7 @@ struct FusedArgs {
   tword_t* v;       // [kCopies][P][r]           A_down h
   // grid layout (filled by the launcher)
   int nR, nWA, nBG, nV, nD, base_la, base_gu, base_v, base_dn, total;
+  int defer_down;  // the down workgroups wait before fetching their routed rows
 };
 
 struct FusedWs {

@@ -598,6 +598,8 @@ struct DGeo {
   static_assert(NS % LPR == 0 && SL >= 1, "down geometry");
 };
 
+constexpr int kDownDeferSleep = 110;  // x 64 shader clocks
+
 template <int H, int I>
 __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* lds_hs, int* lds_he,
                           float* lds_v, float* lds_wt, int* lds_idx) {
@@ -656,6 +658,11 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
   }
   __syncthreads();
   FUSED_MARK(1);
+  // With many routed gate/up rows in flight (the large blocks: defer_down),
+  // this role waits ~3 us before it fetches its rows and starts polling for
+  // h: h cannot be complete earlier, and the fetch would only take HBM
+  // bandwidth from the gate/up rows that the step is waiting for.
+  if (a.defer_down) __builtin_amdgcn_s_sleep(kDownDeferSleep);
   // resident blobs are fetched at once; if any blob is the host copy, one
   // modeled latency precedes all of this thread's host reads
   uint32_t missed = 0;
@@ -862,6 +869,7 @@ static hipError_t launch_fused_t(FusedArgs a, hipStream_t st) {
   a.base_v = a.base_gu + P * a.nBG;
   a.base_dn = a.base_v + P * a.nV;
   a.total = a.base_dn + a.nD;
+  a.defer_down = uint64_t(a.T) * a.K * uint64_t(a.I) * a.H >= kDeferDownBytes;
   hipLaunchKernelGGL((k_fused_decode<H, I>), dim3(a.total), dim3(256), 0, st, a);
   return hipGetLastError();
 }
