@@ -733,8 +733,10 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
   // below; checked (and reloaded if not yet published) before its use
   const int nv = P * r;
   const tword_t* v_c = a.v + size_t(c) * P * r;
-  tword_t vw = 0;
-  if (r > 0) vw = ld_dev(&v_c[min(tid, nv - 1)]);
+  // (without LoRA the second read below takes a logit word instead, unused)
+  const tword_t* vsrc = r > 0 ? v_c + min(tid, nv - 1) : a.logits;
+  tword_t vw = 0, vw2 = 0;
+  if (r > 0) vw = ld_dev(vsrc);
   {
     // h words to LDS, and the sum of each 16-column block (8 consecutive
     // words, held by 8 consecutive threads) for the affine term
@@ -777,12 +779,21 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
       const int bidx = p * NB + sl;
       y[p] += ldexpf(fmaf(sc, acc, (bi - 128.0f * sc) * lds_hs[bidx]), lds_he[bidx]);
     }
+    if (p == 1) {
+      // a second read of v part way through the rows (the first often comes
+      // back before v is published), so that a valid copy returns about when
+      // the rows are done rather than one memory round trip after them
+      __builtin_amdgcn_sched_barrier(0);
+      vw2 = ld_dev(vsrc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   FUSED_MARK(4);
   if (r > 0) {  // lambda B_down v
+    vw = has_tag(vw, tag) ? vw : vw2;
     for (unsigned n = 0;; ++n) {
       if (round_done(a, tid >= nv || has_tag(vw, tag), n)) break;
-      vw = ld_dev(&v_c[min(tid, nv - 1)]);
+      vw = ld_dev(vsrc);
     }
     if (tid < nv) lds_v[(tid / r) * kMaxR + tid % r] = wf(vw);
     __syncthreads();
