@@ -78,22 +78,26 @@ __global__ void __launch_bounds__(256) k_router_logits(const int8_t* __restrict_
 
 constexpr int kMaxTopkSplits = 4;  // K splits of the router GEMM summed by k_topk
 
+constexpr int kTopkTokens = 16;  // tokens (waves) per top-K workgroup
+
 // One wave per token: K rounds of wave argmax over (logit desc, index asc),
 // then the routing weights and the shared gate.  With plog the logits are
 // first summed from the K splits of the router GEMM (split order, then the
-// bias) and stored.  MP logits per lane (E <= 64 MP).  grid ceil(T/4), block 256.
+// bias) and stored.  MP logits per lane (E <= 64 MP).  With hist, the
+// workgroup counts its (token, slot) pairs per chunk and expert in LDS first
+// and adds each nonzero count to the chunk histogram once: under a skewed
+// routing one expert takes a large share of the pairs, and one global add
+// per pair made those adds queue on a few addresses.  grid
+// ceil(T / kTopkTokens), block 64 kTopkTokens.
 template <int MP>
-__global__ void __launch_bounds__(256) k_topk(float* __restrict__ logits,
-                                               float* __restrict__ sg_logit, int T, int E,
-                                               int K, int n_shared, int norm,
-                                               int32_t* __restrict__ idx, float* __restrict__ w,
-                                               float* __restrict__ sw,
-                                               const float* __restrict__ plog, int nks,
-                                               const float* __restrict__ bias,
-                                               int32_t* __restrict__ hist) {
+__device__ __forceinline__ void topk_token(float* __restrict__ logits,
+                                           float* __restrict__ sg_logit, int t, int T, int E,
+                                           int K, int n_shared, int norm,
+                                           int32_t* __restrict__ idx, float* __restrict__ w,
+                                           float* __restrict__ sw,
+                                           const float* __restrict__ plog, int nks,
+                                           const float* __restrict__ bias, int* lhist, int c0) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
   float* l = logits + size_t(t) * E;
   float v[MP];
 #pragma unroll
@@ -157,9 +161,40 @@ __global__ void __launch_bounds__(256) k_topk(float* __restrict__ logits,
     w[size_t(t) * K + lane] = mine / denom;
     // per-chunk expert histogram of the (token, slot) pairs for the grouping
     // (integer adds: the counts do not depend on their order)
-    if (hist) atomicAdd(&hist[size_t((t * K + lane) / kGroupChunk) * E + mine_e], 1);
+    if (lhist) atomicAdd(&lhist[((t * K + lane) / kGroupChunk - c0) * E + mine_e], 1);
   }
   if (n_shared && lane == 0) sw[t] = sigmoid_f(sgl);
+}
+
+template <int MP>
+__global__ void __launch_bounds__(64 * kTopkTokens) k_topk(float* __restrict__ logits,
+                                                            float* __restrict__ sg_logit, int T,
+                                                            int E, int K, int n_shared, int norm,
+                                                            int32_t* __restrict__ idx,
+                                                            float* __restrict__ w,
+                                                            float* __restrict__ sw,
+                                                            const float* __restrict__ plog,
+                                                            int nks, const float* __restrict__ bias,
+                                                            int32_t* __restrict__ hist) {
+  // the workgroup's pairs lie in at most two chunks (kTopkTokens K <= kGroupChunk)
+  __shared__ int lhist[2 * kMaxE];
+  const int t0 = blockIdx.x * kTopkTokens, t = t0 + (threadIdx.x >> 6);
+  const int c0 = (t0 * K) / kGroupChunk;
+  if (hist) {
+    for (int i = threadIdx.x; i < 2 * E; i += 64 * kTopkTokens) lhist[i] = 0;
+    __syncthreads();
+  }
+  if (t < T)
+    topk_token<MP>(logits, sg_logit, t, T, E, K, n_shared, norm, idx, w, sw, plog, nks, bias,
+                   hist ? lhist : nullptr, c0);
+  if (hist) {
+    __syncthreads();
+    const int nch = (T * K + kGroupChunk - 1) / kGroupChunk;
+    for (int i = threadIdx.x; i < 2 * E; i += 64 * kTopkTokens) {
+      const int v = lhist[i], c = c0 + i / E;
+      if (v && c < nch) atomicAdd(&hist[size_t(c) * E + i % E], v);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -199,12 +234,14 @@ hipError_t launch_topk(float* logits, float* sg_logit, int T, int E, int K, int 
                        int norm, int32_t* idx, float* w, float* sw, hipStream_t st,
                        const float* plog, int nks, const float* bias, int32_t* hist) {
   if (plog && (nks < 1 || nks > kMaxTopkSplits)) return hipErrorInvalidValue;
+  static_assert(kTopkTokens * kMaxK <= kGroupChunk, "a workgroup's pairs span at most two chunks");
+  const dim3 grid((T + kTopkTokens - 1) / kTopkTokens), block(64 * kTopkTokens);
   if (E <= 256)  // four logits per lane
-    hipLaunchKernelGGL(k_topk<4>, dim3((T + 3) / 4), dim3(256), 0, st, logits, sg_logit, T, E, K,
-                       n_shared, norm, idx, w, sw, plog, nks, bias, hist);
+    hipLaunchKernelGGL(k_topk<4>, grid, block, 0, st, logits, sg_logit, T, E, K, n_shared, norm,
+                       idx, w, sw, plog, nks, bias, hist);
   else
-    hipLaunchKernelGGL(k_topk<kMaxE / 64>, dim3((T + 3) / 4), dim3(256), 0, st, logits, sg_logit,
-                       T, E, K, n_shared, norm, idx, w, sw, plog, nks, bias, hist);
+    hipLaunchKernelGGL(k_topk<kMaxE / 64>, grid, block, 0, st, logits, sg_logit, T, E, K,
+                       n_shared, norm, idx, w, sw, plog, nks, bias, hist);
   return hipGetLastError();
 }
 
