@@ -149,6 +149,12 @@ __device__ __forceinline__ int group_of_tile(const int32_t* tstart, int G, int m
   return lo;
 }
 
+// v, or zeros when !keep (bit operations, no branch)
+__device__ __forceinline__ uint4 and_mask(uint4 v, bool keep) {
+  const uint32_t m = keep ? ~0u : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
 // 16 int8 codes -> 16 bf16 (exact)
 __device__ __forceinline__ void int8x16_to_bf16(const uint4 q, uint4& lo, uint4& hi) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -245,30 +251,43 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < C::NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // register staging of one chunk
-  uint4 ra[C::A_SEGS];
-  float4 rh[kH16 ? 2 * C::A_SEGS : 1];  // fp32 h segments (LoRA-A of down)
+  // register staging of a chunk, two chunks in flight (stages 0 and 1)
+  constexpr int H_SEGS = kH16 ? 2 * C::A_SEGS : 1;  // fp32 h segments (LoRA-A of down)
   // B staging: int4 -> 16B codes + scale/bias; int8 -> 16B codes; bf16 -> 16B
   constexpr int B_SEGS_INT8 = (BN * 4 + 255) / 256;   // 16B = 16 codes
   constexpr int B_SEGS_BF16 = (BN * 8 + 255) / 256;   // 16B = 8 bf16
   constexpr int B_SEGS = (MODE == kRouter) ? B_SEGS_INT8 : B_SEGS_BF16;
-  uint4 rb[B_SEGS];
+  struct Stage {
+    uint4 ra[C::A_SEGS];
+    float4 rh[H_SEGS];
+    uint4 rb[B_SEGS];
+    float rs[B_SEGS];  // router: the fp32 group scale of the column
+  };
+  Stage st0, st1;
 
-  auto load_chunk = [&](int c) {
+  // whether B staging column n holds a LoRA-A row (else it is zeroed)
+  auto lora_b_ok = [&](int n) {
+    return n < BN && (MODE == kLoraGU ? (n & 15) : (n & 31)) < a.r;
+  };
+  // Every load is issued unconditionally (operands outside the tile read
+  // valid memory of the same array; store_chunk zeroes them), so that the
+  // waits before a chunk's use cover only that chunk's loads.
+  auto load_chunk = [&](Stage& st, int c) {
+    uint4(&ra)[C::A_SEGS] = st.ra;
+    float4(&rh)[H_SEGS] = st.rh;
+    uint4(&rb)[B_SEGS] = st.rb;
     const int k0 = c * BK;
     if constexpr (kH16) {
 #pragma unroll
       for (int i = 0; i < C::A_SEGS; ++i) {
-        const float* src = hrow[i];
-        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-        rh[2 * i] = src ? *reinterpret_cast<const float4*>(src + k0 + 8 * aseg[i]) : z;
-        rh[2 * i + 1] = src ? *reinterpret_cast<const float4*>(src + k0 + 8 * aseg[i] + 4) : z;
+        const float* src = (hrow[i] ? hrow[i] : a.hf) + k0 + 8 * aseg[i];
+        rh[2 * i] = *reinterpret_cast<const float4*>(src);
+        rh[2 * i + 1] = *reinterpret_cast<const float4*>(src + 4);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < C::A_SEGS; ++i) {
-        const uint16_t* src = arow[i];
-        ra[i] = src ? *reinterpret_cast<const uint4*>(src + k0 + 8 * aseg[i]) : make_uint4(0, 0, 0, 0);
+        ra[i] = *reinterpret_cast<const uint4*>((arow[i] ? arow[i] : a.x) + k0 + 8 * aseg[i]);
       }
     }
     if (MODE == kRouter) {
@@ -277,44 +296,31 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
         const int sidx = tid + 256 * i;
         const int n = sidx >> 2, seg = sidx & 3;
         const int R = n0 + n;
-        const int8_t* q = nullptr;
-        if (n < BN && R < Nrows) q = (R < a.E) ? a.rq + size_t(R) * a.H : a.sq;
-        rb[i] = q ? *reinterpret_cast<const uint4*>(q + k0 + 16 * seg) : make_uint4(0, 0, 0, 0);
+        const int8_t* q = !(n < BN && R < Nrows) ? a.rq : (R < a.E) ? a.rq + size_t(R) * a.H : a.sq;
+        rb[i] = *reinterpret_cast<const uint4*>(q + k0 + 16 * seg);
+        // the column's scale for this chunk (rows past the tile read row 0's)
+        const float* sp = (R < a.E && n < BN) ? a.rs + size_t(R) * (a.H / 64)
+                                              : (R < Nrows && n < BN ? a.ss : a.rs);
+        st.rs[i] = sp[c];
       }
     } else {
+      // (no LoRA-A launch without LoRA: r >= 1, so row 0 of each factor exists)
+      const uint16_t* base = reinterpret_cast<const uint16_t*>(blob + (MODE == kLoraGU ? a.L.a_gu : a.L.a_dn));
 #pragma unroll
       for (int i = 0; i < B_SEGS_BF16; ++i) {
         const int sidx = tid + 256 * i;
         const int n = sidx >> 3, seg = sidx & 7;
-        const uint16_t* src = nullptr;
-        if (n < BN) {
-          // gate/up: output column n computes row (n & 15) of A_gate (n < 16)
-          // or A_up (n >= 16), summed over K splits and split into hi/lo
-          // bf16 parts by k_lora_reduce; down: row (n & 31) of A_down, each
-          // row appearing twice so the epilogue can store a hi and a lo part
-          if (MODE == kLoraGU) {
-            const int rr = n & 15;
-            if (rr < a.r)
-              src = reinterpret_cast<const uint16_t*>(blob + a.L.a_gu) +
-                    (size_t(n >= 16 ? a.r : 0) + rr) * a.H;
-          } else if ((n & 31) < a.r) {
-            src = reinterpret_cast<const uint16_t*>(blob + a.L.a_dn) + size_t(n & 31) * a.I;
-          }
-        }
-        // (through the global address space: src comes from a blob address
-        // read from memory and would otherwise load through flat instructions)
-        rb[i] = src ? gload16(src + k0 + 8 * seg) : make_uint4(0, 0, 0, 0);
+        // gate/up: output column n computes row (n & 15) of A_gate (n < 16)
+        // or A_up (n >= 16), summed over K splits and split into hi/lo bf16
+        // parts by k_lora_reduce; down: row (n & 31) of A_down, each row
+        // appearing twice so the epilogue can store a hi and a lo part
+        const size_t row = (MODE == kLoraGU) ? size_t(n >= 16 ? a.r : 0) + (n & 15) : size_t(n & 31);
+        const size_t ld = (MODE == kLoraGU) ? size_t(a.H) : size_t(a.I);
+        // (through the global address space: the blob address is read from
+        // memory and would otherwise load through flat instructions)
+        rb[i] = gload16(base + (lora_b_ok(n) ? row * ld : 0) + k0 + 8 * seg);
       }
     }
-  };
-
-  // router: fp32 group scale per output column, applied per chunk (never
-  // rounded into the bf16 operand)
-  auto router_scale = [&](int n, int c) -> float {
-    const int R = n0 + n;
-    if (R < a.E) return a.rs[size_t(R) * (a.H / 64) + c];
-    if (R < Nrows) return a.ss[c];
-    return 0.f;
   };
 
   // router: fp32 scale of each output column for the current chunk (the
@@ -322,7 +328,10 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) float Ssc[BN];
   constexpr bool kPost = (MODE == kRouter);
 
-  auto store_chunk = [&](int c) {
+  auto store_chunk = [&](Stage& st, int c) {
+    uint4(&ra)[C::A_SEGS] = st.ra;
+    float4(&rh)[H_SEGS] = st.rh;
+    uint4(&rb)[B_SEGS] = st.rb;
     if constexpr (kH16) {  // fp16(h * 2^-e), as the down GEMM reads it
 #pragma unroll
       for (int i = 0; i < C::A_SEGS; ++i) {
@@ -334,6 +343,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
         const f16x2_t p3 = {_Float16(ldexpf(v1.z, -e)), _Float16(ldexpf(v1.w, -e))};
         ra[i] = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
                            __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+        ra[i] = and_mask(ra[i], hrs[i] >= 0);  // a row past the tile is zero
         if (hrs[i] >= 0) {
           *reinterpret_cast<uint4*>(a.hs_out + size_t(hrs[i]) * a.I + c * BK + 8 * aseg[i]) = ra[i];
           if (c == 0 && aseg[i] == 0) a.eh_out[hrs[i]] = e;
@@ -343,14 +353,15 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < C::A_SEGS; ++i) {
       const int sidx = tid + 256 * i;
-      *reinterpret_cast<uint4*>(&As[(sidx >> 3) * LDS_STRIDE + 8 * (sidx & 7)]) = ra[i];
+      const bool ok = kH16 || arow[i] != nullptr;  // rows past the tile are zero
+      *reinterpret_cast<uint4*>(&As[(sidx >> 3) * LDS_STRIDE + 8 * (sidx & 7)]) = and_mask(ra[i], ok);
     }
     if (MODE == kLoraGU || MODE == kLoraD) {
 #pragma unroll
       for (int i = 0; i < B_SEGS_BF16; ++i) {
         const int sidx = tid + 256 * i;
         if ((sidx >> 3) < BN) {
-          uint4 v = rb[i];
+          uint4 v = and_mask(rb[i], lora_b_ok(sidx >> 3));
           if (kF16)  // bf16 LoRA factors -> fp16 operands
             v = make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z),
                            bf16x2_to_f16x2(v.w));
@@ -363,12 +374,14 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
         const int sidx = tid + 256 * i;
         const int n = sidx >> 2;
         if (n < BN) {
+          const bool ok = n0 + n < Nrows;  // columns past the router rows are zero
           uint4 lo, hi;
-          int8x16_to_bf16(rb[i], lo, hi);
+          int8x16_to_bf16(and_mask(rb[i], ok), lo, hi);
           uint16_t* dst = &Bs[n * LDS_STRIDE + 16 * (sidx & 3)];
           *reinterpret_cast<uint4*>(dst) = lo;
           *reinterpret_cast<uint4*>(dst + 8) = hi;
-          if ((sidx & 3) == 0) Ssc[n] = router_scale(n, c);
+          // (the column's four threads write the same value)
+          Ssc[n] = __uint_as_float(__float_as_uint(st.rs[i]) & (ok ? ~0u : 0u));
         }
       }
     }
@@ -377,12 +390,8 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   // router: split-K over blockIdx.y (partial sums of disjoint chunk ranges)
   const int ks = blockIdx.y, nks = gridDim.y;
   const int c0 = ks * nchunks / nks, c1 = (ks + 1) * nchunks / nks;
-  load_chunk(c0);
-  for (int c = c0; c < c1; ++c) {
-    __syncthreads();
-    store_chunk(c);
-    __syncthreads();
-    if (c + 1 < c1) load_chunk(c + 1);
+  const int clast = max(c1 - 1, c0);  // prefetches past the range reload its last chunk (unused)
+  auto compute = [&]() {
     const bool post = kPost;
     f32x4_t part[C::MB][C::NB];
 #pragma unroll
@@ -390,16 +399,16 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < C::NB; ++j) part[i][j] = post ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[i][j];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int kk = 0; kk < 2; ++kk) {
       uint4 af[C::MB], bfr[C::NB];
 #pragma unroll
       for (int i = 0; i < C::MB; ++i)
         af[i] = *reinterpret_cast<const uint4*>(
-            &As[(wm0 + 16 * i + (lane & 15)) * LDS_STRIDE + 32 * ks + 8 * (lane >> 4)]);
+            &As[(wm0 + 16 * i + (lane & 15)) * LDS_STRIDE + 32 * kk + 8 * (lane >> 4)]);
 #pragma unroll
       for (int j = 0; j < C::NB; ++j)
         bfr[j] = *reinterpret_cast<const uint4*>(
-            &Bs[(wn0 + 16 * j + (lane & 15)) * LDS_STRIDE + 32 * ks + 8 * (lane >> 4)]);
+            &Bs[(wn0 + 16 * j + (lane & 15)) * LDS_STRIDE + 32 * kk + 8 * (lane >> 4)]);
 #pragma unroll
       for (int i = 0; i < C::MB; ++i)
 #pragma unroll
@@ -428,6 +437,24 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
       for (int i = 0; i < C::MB; ++i)
 #pragma unroll
         for (int j = 0; j < C::NB; ++j) acc[i][j] = part[i][j];
+    }
+  };
+  // chunk c from a stage to LDS, the stage's next chunk (two ahead) into its
+  // registers, then the MFMAs of chunk c; the other stage's loads stay in flight
+  load_chunk(st0, c0);
+  load_chunk(st1, min(c0 + 1, clast));
+  for (int c = c0; c < c1; c += 2) {
+    __syncthreads();
+    store_chunk(st0, c);
+    __syncthreads();
+    load_chunk(st0, min(c + 2, clast));
+    compute();
+    if (c + 1 < c1) {
+      __syncthreads();
+      store_chunk(st1, c + 1);
+      __syncthreads();
+      load_chunk(st1, min(c + 3, clast));
+      compute();
     }
   }
 
