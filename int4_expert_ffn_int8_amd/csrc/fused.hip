@@ -757,18 +757,32 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
   for (int k = 0; k < MAXE; ++k)
     if (tid + 256 * k < nblk) lds_he[tid + 256 * k] = int(uint32_t(hev[k]));
   __syncthreads();
-  // this lane's part of every pair's output row
+  // this lane's part of every pair's output row; the LDS operands of pair
+  // p + 1 are read before pair p is computed (reads past P are harmless)
+  struct HB { uint4 h0, h1; float hs; int he; };
+  HB cur[SL], nxt[SL];
+  auto ldh = [&](int p, HB (&dst)[SL]) {
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int sl = sub + LPR * s;  // block of 16 columns
+      const uint4* hp = reinterpret_cast<const uint4*>(lds_hh + p * I + 16 * sl);
+      dst[s].h0 = hp[0];
+      dst[s].h1 = hp[1];
+      dst[s].hs = lds_hs[p * NB + sl];
+      dst[s].he = lds_he[p * NB + sl];
+    }
+  };
+  ldh(0, cur);
   float y[kFusedMaxP];
 #pragma unroll
   for (int p = 0; p < kFusedMaxP; ++p) {
     y[p] = 0.f;
     if (p >= P) continue;
+    if (p + 1 < kFusedMaxP) ldh(p + 1, nxt);
 #pragma unroll
     for (int s = 0; s < SL; ++s) {
-      const int sl = sub + LPR * s;  // block of 16 columns
-      const uint4* hp = reinterpret_cast<const uint4*>(lds_hh + p * I + 16 * sl);
-      const uint4 h0 = hp[0], h1 = hp[1];
-      const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+      const uint32_t hw[8] = {cur[s].h0.x, cur[s].h0.y, cur[s].h0.z, cur[s].h0.w,
+                              cur[s].h1.x, cur[s].h1.y, cur[s].h1.z, cur[s].h1.w};
       const uint32_t qw[2] = {q[p][s].x, q[p][s].y};
       float acc = 0.f;
 #pragma unroll
@@ -776,8 +790,11 @@ __device__ void role_down(const FusedArgs& a, int d, uint16_t* lds_hh, float* ld
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) acc = dot2_f16(codes_to_f16x2_biased(qw[dd], s4), hw[4 * dd + s4], acc);
       const float sc = bf16_lo(sbw[p][s]), bi = bf16_hi(sbw[p][s]);
-      const int bidx = p * NB + sl;
-      y[p] += ldexpf(fmaf(sc, acc, (bi - 128.0f * sc) * lds_hs[bidx]), lds_he[bidx]);
+      y[p] += ldexpf(fmaf(sc, acc, (bi - 128.0f * sc) * cur[s].hs), cur[s].he);
+    }
+    if (p + 1 < kFusedMaxP) {
+#pragma unroll
+      for (int s = 0; s < SL; ++s) cur[s] = nxt[s];
     }
     if (p == 1) {
       // a second read of v part way through the rows (the first often comes
