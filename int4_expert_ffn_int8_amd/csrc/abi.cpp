@@ -176,7 +176,6 @@ extern "C" moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_expert
     g.hmax = reinterpret_cast<uint32_t*>(wsb + W.hmax);
     g.hs = hs16;
     g.eh = eh;
-    g.u = g.u_out = reinterpret_cast<uint16_t*>(wsb + W.pu);
     g.ud = g.ud_out = reinterpret_cast<uint16_t*>(wsb + W.pud);
     g.upart = reinterpret_cast<float*>(wsb + W.upart);
     g.y = y;

@@ -442,13 +442,40 @@ __global__ void __launch_bounds__(512, 4) k_expert_gemm(GemmArgs a, int nblk) {
   __syncthreads();
 
   if (a.r > 0) {  // the LoRA chunk, in stage 0's A layout
-    const uint16_t* src = (MODE == kGemmGateUp) ? a.u : a.ud;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int idx = tid + 512 * i, m = idx >> 3, sg = idx & 7;
       const int s = min(row0 + m, row_end - 1);
-      *reinterpret_cast<u32x4_t*>(S0 + kStA + m * 128 + 16 * (sg ^ ((m >> 1) & 7))) =
-          gload<u32x4_t>(src + size_t(s) * kLoraK + 8 * sg);
+      u32x4_t seg;
+      if (MODE == kGemmGateUp) {
+        // lambda * (A v) * 2^-ex from the LoRA-A GEMM's K-split partials,
+        // summed in split order: segment sg holds [gate hi | gate lo | up hi
+        // | up lo] entries 8 (sg & 1) .. + 7 of its quarter
+        const int NR = a.gstart[a.E + 1];
+        const int j0 = (sg >= 4 ? 16 : 0) + 8 * (sg & 1);
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < kLoraSplit; ++k) {
+          const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.upart + (size_t(k) * NR + s) * 32 + j0);
+          const f32x4_t p0 = gload<f32x4_t>(src), p1 = gload<f32x4_t>(src + 1);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[q] += p0[q];
+            v[4 + q] += p1[q];
+          }
+        }
+        const bool lo_part = (sg >> 1) & 1;
+        uint32_t hb[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float lv = (8 * (sg & 1) + q < a.r) ? ldexpf(a.lam * v[q], -row_e[m]) : 0.f;
+          const uint16_t hi = f32_to_bf16(lv);
+          hb[q] = lo_part ? f32_to_bf16(lv - bf16_to_f32(hi)) : hi;
+        }
+        seg = u32x4_t{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16)};
+      } else {
+        seg = gload<u32x4_t>(a.ud + size_t(s) * kLoraK + 8 * sg);
+      }
+      *reinterpret_cast<u32x4_t*>(S0 + kStA + m * 128 + 16 * (sg ^ ((m >> 1) & 7))) = seg;
     }
     __syncthreads();
     // Weight side: B[R][rr] as bf16 for the k the lane covers.  Activation

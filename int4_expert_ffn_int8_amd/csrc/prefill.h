@@ -38,8 +38,6 @@ struct GemmArgs {
   const int32_t* eh;          // [NR]
   uint16_t* hs_out;           // where the LoRA-A GEMM of down writes hs (and eh_out eh)
   int32_t* eh_out;
-  const uint16_t* u;          // [NR][64] lambda * (A_g x, A_u x) * 2^-ex as bf16 hi/lo pairs
-  uint16_t* u_out;
   const uint16_t* ud;         // [NR][64] lambda * (A_d h) * 2^-eh as bf16 hi/lo pairs
   uint16_t* ud_out;
   // router GEMM

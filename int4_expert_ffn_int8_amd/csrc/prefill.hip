@@ -312,7 +312,7 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
         const int n = sidx >> 3, seg = sidx & 7;
         // gate/up: output column n computes row (n & 15) of A_gate (n < 16)
         // or A_up (n >= 16), summed over K splits and split into hi/lo bf16
-        // parts by k_lora_reduce; down: row (n & 31) of A_down, each row
+        // parts as the gate/up GEMM stages its LoRA chunk; down: row (n & 31) of A_down, each row
         // appearing twice so the epilogue can store a hi and a lo part
         const size_t row = (MODE == kLoraGU) ? size_t(n >= 16 ? a.r : 0) + (n & 15) : size_t(n & 31);
         const size_t ld = (MODE == kLoraGU) ? size_t(a.H) : size_t(a.I);
@@ -515,26 +515,6 @@ hipError_t launch_group(const int32_t* idx, int T, int K, int E, int32_t* counts
 
 constexpr int kLoraBM = 64;  // rows per LoRA-A workgroup (two per group tile)
 
-// u[s] of the gate/up LoRA chunk from the K-split partials of A_gate x and
-// A_up x (columns 0..15 and 16..31): lambda * (A v) * 2^-ex[token], as
-// [gate hi 0..15 | gate lo 16..31 | up hi 32..47 | up lo 48..63] bf16, ranks
-// past r zero.  grid ceil(NR * 32 / 256).
-__global__ void __launch_bounds__(256) k_lora_reduce(GemmArgs a, int nks) {
-  const int NR = a.gstart[a.E + 1];
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= NR * 32) return;
-  const int s = i >> 5, j = i & 31;
-  float v = 0.f;
-  for (int k = 0; k < nks; ++k) v += a.upart[(size_t(k) * NR + s) * 32 + j];
-  const int rr = j & 15;
-  const float lv = (rr < a.r) ? ldexpf(a.lam * v, -a.ex[token_of(a, s)]) : 0.f;
-  const uint16_t hi = f32_to_bf16(lv);
-  const uint16_t lo = f32_to_bf16(lv - bf16_to_f32(hi));
-  uint16_t* d = a.u_out + size_t(s) * kLoraK + (j >= 16 ? 32 : 0) + rr;
-  d[0] = hi;
-  d[16] = lo;
-}
-
 hipError_t launch_router_gemm(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = 64, BN = 64;
   const int mtn = (a.T + BM - 1) / BM, ntn = (a.E + a.S + BN - 1) / BN;
@@ -576,11 +556,9 @@ hipError_t launch_prefill_experts(const GemmArgs& a, const int32_t* counts, Expe
   hipError_t e = launch_x16_setup(xs, st);
   if (e != hipSuccess) return e;
   const int mt = prefill_max_mtiles(a.T, a.K, a.E, a.S);
-  if (a.r > 0) {  // LoRA-A of gate/up: K split in kLoraSplit, partials summed in order
+  if (a.r > 0)  // LoRA-A of gate/up: K split in kLoraSplit; the gate/up GEMM sums the partials in order
     hipLaunchKernelGGL((k_gemm<kLoraGU, kLoraBM, 32, 2, 2>), dim3(mt * (kPrefillBM / kLoraBM), kLoraSplit),
                        dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_lora_reduce, dim3((NR * 32 + 255) / 256), dim3(256), 0, st, a, kLoraSplit);
-  }
   e = launch_expert_gemm(kGemmGateUp, a, mt, st);
   if (e != hipSuccess) return e;
   if (a.r > 0) {  // LoRA-A of down, which also writes h as fp16 rows with their exponents

@@ -23,7 +23,6 @@ struct WsLayout {
   size_t gstart;      // int32 [E+2]
   size_t tstart;      // int32 [E+2]
   size_t gblob;       // u64 [E+1]
-  size_t pu;          // bf16 [NR, 64]  lambda * LoRA-A of gate/up
   size_t pud;         // bf16 [NR, 64]  lambda * LoRA-A of down (hi/lo pairs)
   size_t upart;       // fp32 [kLoraSplit, NR, 32] K-split partials of the gate/up LoRA-A
   size_t x16;         // fp16 [T, H]    x * 2^-ex (prefill)
@@ -56,7 +55,6 @@ inline WsLayout ws_layout(const moe_dims_t& d, int T, bool prefill) {
   W.gstart = o;     o = align256(o + (prefill ? (E + 2) * 4 : 0));
   W.tstart = o;     o = align256(o + (prefill ? (E + 2) * 4 : 0));
   W.gblob = o;      o = align256(o + (prefill ? (E + 1) * 8 : 0));
-  W.pu = o;         o = align256(o + NR * kLoraK * 2);
   W.pud = o;        o = align256(o + NR * kLoraK * 2);
   W.upart = o;      o = align256(o + size_t(kLoraSplit) * NR * 32 * 4);
   const size_t TP = prefill ? size_t(T) : 0;
