@@ -195,7 +195,28 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   // tile then takes kPrefillBM / BM consecutive workgroups
   constexpr int kSub = (MODE == kRouter) ? 1 : kPrefillBM / BM;
   static_assert(MODE == kRouter || kPrefillBM % BM == 0, "LoRA-A tiles divide the group tiles");
-  const int mt = blockIdx.x / ntn / kSub, nt = blockIdx.x % ntn, sub = (blockIdx.x / ntn) % kSub;
+  int mt, nt, sub, ks, nks;
+  if (MODE == kRouter) {
+    // 1-D grid, workgroup b on XCD b % 8: each XCD takes a contiguous run of
+    // (row tile, K split) units, and the column tiles of a unit, which read
+    // the same slice of x, run on that XCD one after another (its L2 serves
+    // all but the first read of the slice)
+    nks = a.plog ? kRouterSplit : 1;
+    const int units = ((a.T + BM - 1) / BM) * nks, per = (units + 7) / 8;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int unit = xcd * per + slot / ntn;
+    if (slot / ntn >= per || unit >= units) return;
+    mt = unit / nks;
+    ks = unit % nks;
+    nt = slot % ntn;
+    sub = 0;
+  } else {
+    mt = blockIdx.x / ntn / kSub;
+    nt = blockIdx.x % ntn;
+    sub = (blockIdx.x / ntn) % kSub;
+    ks = blockIdx.y;  // split-K over blockIdx.y (partial sums of disjoint chunk ranges)
+    nks = gridDim.y;
+  }
   const int n0 = nt * BN;
   int row0, row_end, g = 0;
   const uint8_t* blob = nullptr;
@@ -387,8 +408,6 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
     }
   };
 
-  // router: split-K over blockIdx.y (partial sums of disjoint chunk ranges)
-  const int ks = blockIdx.y, nks = gridDim.y;
   const int c0 = ks * nchunks / nks, c1 = (ks + 1) * nchunks / nks;
   const int clast = max(c1 - 1, c0);  // prefetches past the range reload its last chunk (unused)
   auto compute = [&]() {
@@ -521,8 +540,10 @@ hipError_t launch_router_gemm(const GemmArgs& a, hipStream_t st) {
   // split K so a few thousand tokens give about 1000 workgroups with short
   // chunk loops; the partial sums are reduced in a fixed order
   const int nks = a.plog ? kRouterSplit : 1;
-  // (the top-K kernel sums the splits)
-  hipLaunchKernelGGL((k_gemm<kRouter, BM, BN, 2, 2>), dim3(mtn * ntn, nks), dim3(256), 0, st, a);
+  // (the top-K kernel sums the splits); one 1-D slot per (row tile, split,
+  // column tile), padded so that every XCD has the same number of slots
+  const int units = mtn * nks;
+  hipLaunchKernelGGL((k_gemm<kRouter, BM, BN, 2, 2>), dim3(8 * ((units + 7) / 8) * ntn), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
