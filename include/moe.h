@@ -216,6 +216,35 @@ MOE_API moe_status_t moe_combine(const moe_dims_t* d, const float* y, const floa
                          const float* shared_w, int32_t T, const uint16_t* residual,
                          uint16_t* out, uint16_t* norm_out, float eps, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * moe_block_prefill: the whole block for a batch of prefill tokens in one
+ * call -- moe_route with grouping, moe_expert_forward on the grouped path,
+ * moe_combine -- with the same arithmetic except for where the expert
+ * outputs are kept: in the workspace, as fp16(y * 2^-e) with one power-of-two
+ * exponent e per (token, slot) row instead of fp32, which halves the bytes the
+ * down GEMM writes and the combine reads.  e comes from a bound on the down
+ * projection's outputs that moe_pack_expert stores in each blob, so no value
+ * can overflow, and each y keeps fp16's 11-bit significand (relative rounding
+ * 2^-11; values below 2^-29 of the bound lose precision as subnormals).
+ * [P2] "SSD 专家卸载 · Prerouter 路由预测", prefill/decode paragraph: prefill
+ * batches the whole layer's computation.
+ *   gate_q .. logit_bias, x, T: as in moe_route (logit_bias may be NULL).
+ *   routed, shared_blob: as in moe_expert_forward.
+ *   residual, out, norm_out, eps: as in moe_combine.
+ *   topk_idx device int32 [T, K], topk_w fp32 [T, K]: the routing (outputs).
+ *   ws     moe_block_prefill_workspace_bytes(d, T) bytes; calls that share
+ *          one must be ordered on one stream.
+ * T == 0 is valid and enqueues nothing. */
+MOE_API size_t moe_block_prefill_workspace_bytes(const moe_dims_t* d, int32_t T);
+MOE_API moe_status_t moe_block_prefill(const moe_dims_t* d, const int8_t* gate_q,
+                                       const float* gate_s, const int8_t* sgate_q,
+                                       const float* sgate_s, const float* logit_bias,
+                                       const moe_experts_t* routed, const void* shared_blob,
+                                       const uint16_t* x, int32_t T, const uint16_t* residual,
+                                       int32_t* topk_idx, float* topk_w, uint16_t* out,
+                                       uint16_t* norm_out, float eps, void* ws, size_t ws_bytes,
+                                       void* stream);
+
 /* moe_rmsnorm: out[t] = bf16(h[t] / sqrt(mean(h[t]^2) + eps)), unit gain.
  * h, out device bf16 [T, H] (may alias). */
 MOE_API moe_status_t moe_rmsnorm(const uint16_t* h, int32_t T, int32_t H, float eps, uint16_t* out,

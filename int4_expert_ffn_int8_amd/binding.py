@@ -58,6 +58,10 @@ _SIGS = {
     "moe_combine": (c_i32, [ctypes.POINTER(MoeDims), c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp,
                             c_f32, c_vp]),
     "moe_rmsnorm": (c_i32, [c_vp, c_i32, c_i32, c_f32, c_vp, c_vp]),
+    "moe_block_prefill_workspace_bytes": (c_sz, [ctypes.POINTER(MoeDims), c_i32]),
+    "moe_block_prefill": (c_i32, [ctypes.POINTER(MoeDims), c_vp, c_vp, c_vp, c_vp, c_vp,
+                                  ctypes.POINTER(MoeExperts), c_vp, c_vp, c_i32, c_vp, c_vp, c_vp,
+                                  c_vp, c_vp, c_f32, c_vp, c_sz, c_vp]),
     "moe_block_decode_workspace_bytes": (c_sz, [ctypes.POINTER(MoeDims), c_i32]),
     "moe_workspace_init": (c_i32, [c_vp, c_sz, c_vp]),
     "moe_block_decode": (c_i32, [ctypes.POINTER(MoeDims), c_vp, c_vp, c_vp, c_vp,
@@ -98,6 +102,7 @@ _SIGS = {
 HEADER_SYMBOLS = [
     "moe_last_error", "moe_expert_blob_bytes", "moe_pack_expert", "moe_workspace_bytes",
     "moe_route", "moe_expert_forward", "moe_combine", "moe_rmsnorm",
+    "moe_block_prefill_workspace_bytes", "moe_block_prefill",
     "moe_block_decode_workspace_bytes", "moe_workspace_init", "moe_block_decode",
     "moe_block_decode_exec", "moe_block_decode_noalloc",
     "prerouter_workspace_bytes", "prerouter_predict", "prerouter_predict_feat",
@@ -220,6 +225,23 @@ def moe_combine(d, y, topk_w, shared_w, T, residual, out, norm_out=None, eps=1e-
 
 def moe_rmsnorm(h, T, H, eps, out, stream=None) -> None:
     _check(load().moe_rmsnorm(ptr(h), T, H, eps, ptr(out), stream_ptr(stream)))
+
+
+def moe_block_prefill_workspace_bytes(d: MoeDims, T: int) -> int:
+    return int(load().moe_block_prefill_workspace_bytes(ctypes.byref(d), T))
+
+
+def moe_block_prefill(d, gate_q, gate_s, sgate_q, sgate_s, logit_bias, routed: MoeExperts,
+                      shared_blob, x, T, residual, topk_idx, topk_w, out, norm_out, eps, ws,
+                      stream=None) -> None:
+    """route + experts + combine for T prefill tokens in one call; the expert
+    outputs stay in the workspace (fp16 with a power-of-two exponent per row)."""
+    _check(load().moe_block_prefill(ctypes.byref(d), ptr(gate_q), ptr(gate_s), ptr(sgate_q),
+                                    ptr(sgate_s), ptr(logit_bias), ctypes.byref(routed),
+                                    ptr(shared_blob), ptr(x), T, ptr(residual), ptr(topk_idx),
+                                    ptr(topk_w), ptr(out), ptr(norm_out), eps, ptr(ws),
+                                    ws.numel() * ws.element_size() if ws is not None else 0,
+                                    stream_ptr(stream)))
 
 
 def prerouter_workspace_bytes(D: int, E: int, T: int) -> int:

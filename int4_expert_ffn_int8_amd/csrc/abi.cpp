@@ -115,12 +115,15 @@ extern "C" moe_status_t moe_route(const moe_dims_t* d, const int8_t* gate_q, con
                     fn);
 }
 
-extern "C" moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_experts_t* routed,
-                                           const void* shared_blob, const uint16_t* x, int32_t T,
-                                           const int32_t* topk_idx, const int32_t* counts,
-                                           const int32_t* offsets, const int32_t* perm, float* y,
-                                           void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "moe_expert_forward";
+namespace {
+
+// moe_expert_forward; with y16/ey set (prefill path only) the down GEMM
+// writes the compact expert outputs of moe_block_prefill instead of y.
+moe_status_t expert_forward(const moe_dims_t* d, const moe_experts_t* routed,
+                            const void* shared_blob, const uint16_t* x, int32_t T,
+                            const int32_t* topk_idx, const int32_t* counts, const int32_t* offsets,
+                            const int32_t* perm, float* y, uint16_t* y16, int32_t* ey, void* ws,
+                            size_t ws_bytes, void* stream, const char* fn) {
   moe_status_t st = check_dims(d, fn);
   if (st != MOE_OK) return st;
   if (T < 0) return fail(MOE_EINVAL, "%s: T=%d is negative", fn, T);
@@ -137,7 +140,7 @@ extern "C" moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_expert
   if (routed->n_slots < 1) return fail(MOE_EINVAL, "%s: n_slots=%d", fn, routed->n_slots);
   if (d->n_shared && !shared_blob) return fail(MOE_EINVAL, "%s: n_shared=1 needs shared_blob", fn);
   if (T == 0) return MOE_OK;
-  if (!x || !topk_idx || !y) return fail(MOE_EINVAL, "%s: null x, topk_idx or y", fn);
+  if (!x || !topk_idx || !(y || y16)) return fail(MOE_EINVAL, "%s: null x, topk_idx or y", fn);
   const WsLayout W = ws_layout(*d, T, group);
   if (!ws || ws_bytes < W.total)
     return fail(MOE_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, W.total);
@@ -179,6 +182,8 @@ extern "C" moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_expert
     g.ud = g.ud_out = reinterpret_cast<uint16_t*>(wsb + W.pud);
     g.upart = reinterpret_cast<float*>(wsb + W.upart);
     g.y = y;
+    g.y16 = y16;
+    g.ey = ey;
     return hip_status(launch_prefill_experts(g, counts, src,
                                              static_cast<const uint8_t*>(shared_blob), x16, ex,
                                              hs16, eh, static_cast<hipStream_t>(stream)),
@@ -206,6 +211,17 @@ extern "C" moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_expert
   return hip_status(launch_decode(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+}  // namespace
+
+extern "C" moe_status_t moe_expert_forward(const moe_dims_t* d, const moe_experts_t* routed,
+                                           const void* shared_blob, const uint16_t* x, int32_t T,
+                                           const int32_t* topk_idx, const int32_t* counts,
+                                           const int32_t* offsets, const int32_t* perm, float* y,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  return expert_forward(d, routed, shared_blob, x, T, topk_idx, counts, offsets, perm, y, nullptr,
+                        nullptr, ws, ws_bytes, stream, "moe_expert_forward");
+}
+
 extern "C" moe_status_t moe_combine(const moe_dims_t* d, const float* y, const float* topk_w,
                                     const float* shared_w, int32_t T, const uint16_t* residual,
                                     uint16_t* out, uint16_t* norm_out, float eps, void* stream) {
@@ -231,6 +247,51 @@ extern "C" moe_status_t moe_rmsnorm(const uint16_t* h, int32_t T, int32_t H, flo
   if (T == 0) return MOE_OK;
   if (!h || !out) return fail(MOE_EINVAL, "%s: null pointer", fn);
   return hip_status(launch_rmsnorm(h, T, H, eps, out, static_cast<hipStream_t>(stream)), fn);
+}
+
+// ---------------------------------------------------------------------------
+// one-call prefill block
+// ---------------------------------------------------------------------------
+extern "C" size_t moe_block_prefill_workspace_bytes(const moe_dims_t* d, int32_t T) {
+  if (check_dims(d, "moe_block_prefill_workspace_bytes") != MOE_OK || T < 0) return 0;
+  return block_prefill_layout(*d, T).total;
+}
+
+extern "C" moe_status_t moe_block_prefill(const moe_dims_t* d, const int8_t* gate_q,
+                                          const float* gate_s, const int8_t* sgate_q,
+                                          const float* sgate_s, const float* logit_bias,
+                                          const moe_experts_t* routed, const void* shared_blob,
+                                          const uint16_t* x, int32_t T, const uint16_t* residual,
+                                          int32_t* topk_idx, float* topk_w, uint16_t* out,
+                                          uint16_t* norm_out, float eps, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  const char* fn = "moe_block_prefill";
+  moe_status_t st = check_dims(d, fn);
+  if (st != MOE_OK) return st;
+  if (T < 0) return fail(MOE_EINVAL, "%s: T=%d is negative", fn, T);
+  if (T == 0) return MOE_OK;
+  if (!x || !topk_idx || !topk_w || !out) return fail(MOE_EINVAL, "%s: null x or output pointer", fn);
+  if (norm_out && !(eps >= 0.f && isfinite(eps)))
+    return fail(MOE_EINVAL, "%s: eps must be finite and >= 0", fn);
+  const BlockPrefillLayout P = block_prefill_layout(*d, T);
+  if (!ws || ws_bytes < P.total)
+    return fail(MOE_EWORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, P.total);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  int32_t* counts = reinterpret_cast<int32_t*>(wsb + P.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(wsb + P.offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(wsb + P.perm);
+  float* shared_w = d->n_shared ? reinterpret_cast<float*>(wsb + P.shared_w) : nullptr;
+  uint16_t* y16 = reinterpret_cast<uint16_t*>(wsb + P.y16);
+  int32_t* ey = reinterpret_cast<int32_t*>(wsb + P.ey);
+  st = moe_route(d, gate_q, gate_s, sgate_q, sgate_s, x, T, logit_bias, topk_idx, topk_w, shared_w,
+                 nullptr, counts, offsets, perm, ws, P.W.total, stream);
+  if (st != MOE_OK) return st;
+  st = expert_forward(d, routed, shared_blob, x, T, topk_idx, counts, offsets, perm, nullptr, y16,
+                      ey, ws, P.W.total, stream, fn);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_combine16(y16, ey, topk_w, shared_w, T, d->K, d->n_shared, d->H,
+                                     residual, out, norm_out, eps, static_cast<hipStream_t>(stream)),
+                    fn);
 }
 
 // ---------------------------------------------------------------------------

@@ -88,6 +88,78 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ y,
   }
 }
 
+// k_combine over compact expert outputs: y16 [T][K+S][H] fp16 holding
+// y * 2^-ey with one exponent per (token, slot) row (ey [T][K+S]).  The same
+// sum as k_combine; each power of two is folded into the row's coefficient
+// exactly.
+__global__ void __launch_bounds__(256) k_combine16(const uint16_t* __restrict__ y16,
+                                                    const int32_t* __restrict__ ey,
+                                                    const float* __restrict__ w,
+                                                    const float* __restrict__ sw, int K, int S, int H,
+                                                    const uint16_t* __restrict__ residual,
+                                                    uint16_t* __restrict__ out,
+                                                    uint16_t* __restrict__ norm_out, float eps) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const int KS = K + S;
+  const float g = S ? sw[t] : 0.f;
+  const uint16_t* yt = y16 + size_t(t) * KS * H;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < H / 8; c += 256) {
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < KS; k0 += 4) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)  // rows past KS re-read the last row (not summed)
+        v[u] = *reinterpret_cast<const uint4*>(yt + size_t(min(k0 + u, KS - 1)) * H + 8 * c);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = k0 + u;
+        if (k >= KS) break;
+        const float cf = ldexpf((k < K) ? w[size_t(t) * K + k] : g, ey[size_t(t) * KS + k]);
+        const f16x2_t p[4] = {__builtin_bit_cast(f16x2_t, v[u].x), __builtin_bit_cast(f16x2_t, v[u].y),
+                              __builtin_bit_cast(f16x2_t, v[u].z), __builtin_bit_cast(f16x2_t, v[u].w)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[2 * i] = fmaf(cf, float(p[i][0]), o[2 * i]);
+          o[2 * i + 1] = fmaf(cf, float(p[i][1]), o[2 * i + 1]);
+        }
+      }
+    }
+    if (residual) {
+      const uint4 rv = *reinterpret_cast<const uint4*>(residual + size_t(t) * H + 8 * c);
+      const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[2 * i] += bf16_lo(rw[i]);
+        o[2 * i + 1] += bf16_hi(rw[i]);
+      }
+    }
+    uint32_t ow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t lo = f32_to_bf16(o[2 * i]), hi = f32_to_bf16(o[2 * i + 1]);
+      ow[i] = uint32_t(lo) | (uint32_t(hi) << 16);
+      const float a0 = bf16_to_f32(lo), a1 = bf16_to_f32(hi);
+      ss = fmaf(a0, a0, ss);
+      ss = fmaf(a1, a1, ss);
+    }
+    *reinterpret_cast<uint4*>(out + size_t(t) * H + 8 * c) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  }
+  if (!norm_out) return;
+  const float tot = block_sum_256(ss, red);
+  const float inv = 1.0f / sqrtf(tot / float(H) + eps);
+  for (int c = threadIdx.x; c < H / 8; c += 256) {  // the columns this thread wrote
+    const uint4 ov = *reinterpret_cast<const uint4*>(out + size_t(t) * H + 8 * c);
+    const uint32_t iw[4] = {ov.x, ov.y, ov.z, ov.w};
+    uint32_t nw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      nw[i] = uint32_t(f32_to_bf16(bf16_lo(iw[i]) * inv)) | (uint32_t(f32_to_bf16(bf16_hi(iw[i]) * inv)) << 16);
+    *reinterpret_cast<uint4*>(norm_out + size_t(t) * H + 8 * c) = make_uint4(nw[0], nw[1], nw[2], nw[3]);
+  }
+}
+
 // grid T, block 256
 __global__ void __launch_bounds__(256) k_rmsnorm(const uint16_t* __restrict__ h, int H, float eps,
                                                   uint16_t* __restrict__ out) {
@@ -110,6 +182,15 @@ hipError_t launch_combine(const float* y, const float* w, const float* sw, int T
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, st, y, w, sw, K, S, H, residual, out,
                      norm_out, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine16(const uint16_t* y16, const int32_t* ey, const float* w, const float* sw,
+                            int T, int K, int S, int H, const uint16_t* residual, uint16_t* out,
+                            uint16_t* norm_out, float eps, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_combine16, dim3(T), dim3(256), 0, st, y16, ey, w, sw, K, S, H, residual,
+                     out, norm_out, eps);
   return hipGetLastError();
 }
 

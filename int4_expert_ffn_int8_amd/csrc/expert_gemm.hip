@@ -522,6 +522,18 @@ __global__ void __launch_bounds__(512, 4) k_expert_gemm(GemmArgs a, int nblk) {
     }
   }
 
+  // Compact y (down): fp16(acc * 2^-yc), with yc from the blob's bound on the
+  // down outputs: |acc| <= (W + |lambda| L) 2^15 since every row of h enters
+  // scaled to |h| <= 2^15, so acc * 2^-yc stays below 2^15 whatever the data.
+  float yscale = 1.0f;
+  int yc = 0;
+  if (MODE == kGemmDown && a.y16 != nullptr) {
+    const float* meta = reinterpret_cast<const float*>(blob + a.L.meta);
+    const float bound = gload<float>(meta + kMetaDownW) + fabsf(a.lam) * gload<float>(meta + kMetaDownL);
+    yc = !(bound > 0.f) ? 0 : (bound <= 3.0e38f ? min(ilogbf(bound) + 1, 127) : 127);
+    yscale = ldexpf(1.0f, -yc);
+  }
+
   // ---- epilogue: row scale 2^e, then SwiGLU (gate/up) or the y rows (down)
 #pragma unroll
   for (int i = 0; i < IM; ++i) {
@@ -550,7 +562,7 @@ __global__ void __launch_bounds__(512, 4) k_expert_gemm(GemmArgs a, int nblk) {
         hm = fmaxf(hm, dpp_f<kDppHalfMirror>(hm));
         hm = fmaxf(hm, dpp_f<kDppMirror>(hm));
         if (valid && ln == 0) atomicMax(&a.hmax[s], __float_as_uint(hm));
-      } else {
+      } else if (a.y16 == nullptr) {
         const size_t dest = size_t(row_dst[m]);
         if (valid) {
 #pragma unroll
@@ -559,6 +571,21 @@ __global__ void __launch_bounds__(512, 4) k_expert_gemm(GemmArgs a, int nblk) {
             if (n < Nrows) a.y[dest * a.H + n] = ldexpf(acc[i][j][q], e);
           }
         }
+      } else {
+        // Lane ln holds columns ln (j = 0) and 16 + ln (j = 1) of its row;
+        // neighbouring lanes swap one value so that an even lane stores
+        // columns ln, ln + 1 and an odd lane columns 15 + ln, 16 + ln: one
+        // 4-byte store per lane, 64 contiguous bytes per row.
+        static_assert(JN == 2, "the pairing below covers two 16-column blocks");
+        const size_t dest = size_t(row_dst[m]);
+        const float v0 = acc[i][0][q] * yscale, v1 = acc[i][1][q] * yscale;
+        const float o0 = dpp_f<kDppXor1>(v0), o1 = dpp_f<kDppXor1>(v1);
+        const bool odd = ln & 1;
+        const f16x2_t pv = {_Float16(odd ? o1 : v0), _Float16(odd ? v1 : o0)};
+        const int n = n0 + wn0 + (odd ? 15 + ln : ln);
+        if (valid && n < Nrows)  // n is even and Nrows a multiple of 64: n + 1 < Nrows too
+          *reinterpret_cast<uint32_t*>(a.y16 + dest * a.H + n) = __builtin_bit_cast(uint32_t, pv);
+        if (valid && nt == 0 && wave == 0 && ln == 0) a.ey[dest] = e + yc;  // one writer per row
       }
     }
   }

@@ -54,6 +54,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_combine(const float* y, const float* w, const float* sw, int T, int K, int S,
                           int H, const uint16_t* residual, uint16_t* out, uint16_t* norm_out,
                           float eps, hipStream_t st);
+hipError_t launch_combine16(const uint16_t* y16, const int32_t* ey, const float* w, const float* sw,
+                            int T, int K, int S, int H, const uint16_t* residual, uint16_t* out,
+                            uint16_t* norm_out, float eps, hipStream_t st);
 hipError_t launch_rmsnorm(const uint16_t* h, int T, int H, float eps, uint16_t* out,
                           hipStream_t st);
 

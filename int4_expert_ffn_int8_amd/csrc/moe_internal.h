@@ -40,8 +40,14 @@ struct BlobLayout {
   size_t b_gu;      // bf16 [2I][r]      LoRA B of gate/up, interleaved rows
   size_t a_dn;      // bf16 [r][I]       LoRA A of down
   size_t b_dn;      // bf16 [H][r]       LoRA B of down
+  size_t meta;      // fp32 [2]          bounds of the down projection (see kMetaDown*)
   size_t total;
 };
+// Meta words written by the packer: the largest absolute row sum of the
+// dequantised down weights, max_i sum_j |s q + b|, and a bound on that of the
+// down LoRA product B A, max_i sum_r |B[i, r]| sum_j |A[r, j]|.  With
+// |h| <= M, every down output obeys |y_i| <= (W + |lambda| L) M.
+constexpr int kMetaDownW = 0, kMetaDownL = 1;
 
 inline BlobLayout blob_layout(int H, int I, int r) {
   BlobLayout L;
@@ -54,6 +60,7 @@ inline BlobLayout blob_layout(int H, int I, int r) {
   L.b_gu = o;     o = align256(o + size_t(2) * I * r * 2);
   L.a_dn = o;     o = align256(o + size_t(r) * I * 2);
   L.b_dn = o;     o = align256(o + size_t(H) * r * 2);
+  L.meta = o;     o = align256(o + 2 * 4);
   L.total = o;
   return L;
 }

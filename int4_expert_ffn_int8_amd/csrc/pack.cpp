@@ -112,5 +112,29 @@ extern "C" moe_status_t moe_pack_expert(
     memcpy(out + L.a_dn, A_down, size_t(r) * I * 2);
     memcpy(out + L.b_dn, B_down, size_t(H) * r * 2);
   }
+  // bounds of the down projection's output (moe_internal.h, kMetaDown*)
+  double wmax = 0.0, lmax = 0.0;
+  for (int i = 0; i < H; ++i) {
+    double sum = 0.0;
+    for (int j = 0; j < I; ++j) {
+      const size_t gidx = size_t(i) * Gi + j / kGroup;
+      sum += fabs(bf16_value(s_down[gidx]) * double(q_down[size_t(i) * I + j]) + bf16_value(b_down[gidx]));
+    }
+    wmax = fmax(wmax, sum);
+  }
+  if (r > 0) {
+    double arow[kMaxR];
+    for (int k = 0; k < r; ++k) {
+      arow[k] = 0.0;
+      for (int j = 0; j < I; ++j) arow[k] += fabs(double(bf16_value(A_down[size_t(k) * I + j])));
+    }
+    for (int i = 0; i < H; ++i) {
+      double sum = 0.0;
+      for (int k = 0; k < r; ++k) sum += fabs(double(bf16_value(B_down[size_t(i) * r + k]))) * arow[k];
+      lmax = fmax(lmax, sum);
+    }
+  }
+  const float meta[2] = {float(wmax) * (1.0f + 1e-6f), float(lmax) * (1.0f + 1e-6f)};
+  memcpy(out + L.meta, meta, sizeof(meta));
   return MOE_OK;
 }

@@ -52,8 +52,11 @@ struct GemmArgs {
   float* upart;  // [kLoraSplit][NR][32] partial LoRA-A of gate/up over the K splits
   int32_t* zero;  // router GEMM: nzero ints its first workgroup sets to 0 (grouping histogram)
   int nzero;
-  // down output, [T][K+S][H]
+  // down output, [T][K+S][H]: fp32 y, or (y16 set) fp16 y * 2^-ey with one
+  // exponent per (token, slot) row, ey [T][K+S]
   float* y;
+  uint16_t* y16;
+  int32_t* ey;
 };
 
 hipError_t launch_group(const int32_t* idx, int T, int K, int E, int32_t* counts,

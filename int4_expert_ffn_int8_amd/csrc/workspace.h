@@ -68,4 +68,32 @@ inline WsLayout ws_layout(const moe_dims_t& d, int T, bool prefill) {
   return W;
 }
 
+// Workspace of moe_block_prefill: the route + expert workspace, the routing
+// outputs the caller does not receive, and the compact expert outputs.
+struct BlockPrefillLayout {
+  WsLayout W;       // at offset 0
+  size_t counts;    // int32 [E]
+  size_t offsets;   // int32 [E+1]
+  size_t perm;      // int32 [T*K]
+  size_t shared_w;  // fp32 [T]
+  size_t y16;       // fp16 [T, K+S, H]
+  size_t ey;        // int32 [T, K+S]
+  size_t total;
+};
+
+inline BlockPrefillLayout block_prefill_layout(const moe_dims_t& d, int T) {
+  BlockPrefillLayout P;
+  P.W = ws_layout(d, T, true);
+  const size_t NP = size_t(T) * (d.K + d.n_shared);
+  size_t o = P.W.total;
+  P.counts = o;   o = align256(o + size_t(d.E) * 4);
+  P.offsets = o;  o = align256(o + size_t(d.E + 1) * 4);
+  P.perm = o;     o = align256(o + size_t(T) * d.K * 4);
+  P.shared_w = o; o = align256(o + size_t(T) * 4);
+  P.y16 = o;      o = align256(o + NP * d.H * 2);
+  P.ey = o;       o = align256(o + NP * 4);
+  P.total = o;
+  return P;
+}
+
 }  // namespace moe

@@ -118,6 +118,27 @@ class MoeLayer:
         self.combine(b, residual, norm_out, eps, stream)
         return b["out"]
 
+    # ---- one-call prefill block ----------------------------------------
+    def block_prefill_buffers(self, T: int) -> dict:
+        dv = self.device
+        return {
+            "T": T,
+            "ws": torch.empty((max(B.moe_block_prefill_workspace_bytes(self.d, T), 1),),
+                              dtype=torch.uint8, device=dv),
+            "idx": torch.empty((T, self.K), dtype=torch.int32, device=dv),
+            "w": torch.empty((T, self.K), dtype=torch.float32, device=dv),
+            "out": torch.empty((T, self.H), dtype=torch.int16, device=dv),
+        }
+
+    def block_prefill(self, x, pb, bias=None, residual=None, norm_out=None, eps=1e-6,
+                      routed=None, stream=None):
+        """moe_block_prefill: route + experts + combine in one call, the
+        expert outputs kept compact in the workspace."""
+        B.moe_block_prefill(self.d, self.gate_q, self.gate_s, self.sgate_q, self.sgate_s, bias,
+                            routed or self.experts, self.shared_blob, x, pb["T"], residual,
+                            pb["idx"], pb["w"], pb["out"], norm_out, eps, pb["ws"], stream)
+        return pb["out"]
+
     # ---- fused single-launch decode -----------------------------------
     def fused_buffers(self, T: int) -> dict:
         dv = self.device

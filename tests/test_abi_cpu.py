@@ -34,8 +34,8 @@ def test_library_exports_every_header_symbol(B):
 
 def test_blob_bytes_match_layout(B):
     # 35B-shaped expert: codes 1,572,864 + scale/bias 196,608 + LoRA 245,760
-    assert B.moe_expert_blob_bytes(2048, 512, 16) == 2015232
-    assert B.moe_expert_blob_bytes(256, 128, 4) == 64512
+    assert B.moe_expert_blob_bytes(2048, 512, 16) == 2015232 + 256  # sections + the 256-byte meta
+    assert B.moe_expert_blob_bytes(256, 128, 4) == 64512 + 256
     assert B.moe_expert_blob_bytes(2000, 512, 16) == 0
 
 
@@ -164,7 +164,7 @@ def test_pack_expert_layout_round_trip(B):
     for name, size in [("gu_codes", 2 * I * H // 2), ("gu_sb", 2 * I * (H // 64) * 4),
                        ("dn_codes", H * I // 2), ("dn_sb", H * (I // 64) * 4),
                        ("a_gu", 2 * r * H * 2), ("b_gu", 2 * I * r * 2), ("a_dn", r * I * 2),
-                       ("b_dn", H * r * 2)]:
+                       ("b_dn", H * r * 2), ("meta", 8)]:
         sec[name] = blob[o:o + size]
         o = a256(o + size)
     assert o == blob.size
@@ -187,6 +187,18 @@ def test_pack_expert_layout_round_trip(B):
     assert np.array_equal(a_gu[0], ex["A_gate"]) and np.array_equal(a_gu[1], ex["A_up"])
     assert np.array_equal(sec["a_dn"].view(np.uint16).reshape(r, I), ex["A_down"])
     assert np.array_equal(sec["b_dn"].view(np.uint16).reshape(H, r), ex["B_down"])
+    # meta: bounds of the down projection's outputs, from their definition
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # bf16 bits
+    wd = f(ex["s_down"]).repeat(64, axis=1) * ex["q_down"] + f(ex["b_down"]).repeat(64, axis=1)
+    w_bound = np.abs(wd).sum(axis=1).max()
+    l_bound = (np.abs(f(ex["B_down"])) @ np.abs(f(ex["A_down"])).sum(axis=1)).max()
+    meta = sec["meta"].view(np.float32)
+    assert w_bound <= meta[0] <= w_bound * (1 + 1e-5)
+    assert l_bound <= meta[1] <= l_bound * (1 + 1e-5)
+    # the bound holds: |deq(Q_d) h + B_d (A_d h)| <= (W + L) max|h| for any h
+    h = np.random.default_rng(0).standard_normal(I)
+    y = wd @ h + f(ex["B_down"]) @ (f(ex["A_down"]) @ h)
+    assert np.abs(y).max() <= (meta[0] + meta[1]) * np.abs(h).max()
 
 
 def test_pack_rejects_codes_above_15(B):
