@@ -75,6 +75,33 @@ def test_route_null_pointers_and_workspace(B):
                               None, None, None, None, None, None, None, 0, 0) == 0
 
 
+def test_block_prefill_validation_and_workspace(B):
+    # every check of moe_block_prefill fires before any device work
+    d = B.dims(2048, 512, 256, 4, 16, 1)
+    lib = B.load()
+    T = 3300
+    need = lib.moe_block_prefill_workspace_bytes(B.ctypes.byref(d), T)
+    base = B.moe_workspace_bytes(d, T, True)
+    # the route + expert workspace, then counts, offsets, perm, shared gate,
+    # the compact expert outputs (fp16) and one exponent per (token, slot) row
+    assert need >= base + T * 5 * 2048 * 2 + T * 5 * 4 + T * 4 * 4
+    assert lib.moe_block_prefill_workspace_bytes(B.ctypes.byref(B.dims(2000, 512, 256, 4, 16, 1)), 1) == 0
+    fake = 1 << 40
+    ex = B.MoeExperts(fake, 256, None, None, None, 0)
+    args = lambda x, T, ws, nbytes, eps=1e-6: (B.ctypes.byref(d), fake, fake, fake, fake, None,
+                                               B.ctypes.byref(ex), fake, x, T, None, fake, fake,
+                                               fake, None, eps, ws, nbytes, 0)
+    assert lib.moe_block_prefill(*args(None, 0, None, 0)) == 0          # T == 0: nothing to do
+    assert lib.moe_block_prefill(*args(fake, -1, fake, need)) == 1      # negative T
+    assert lib.moe_block_prefill(*args(None, T, fake, need)) == 1       # null x
+    st = lib.moe_block_prefill(*args(fake, T, fake, need - 1))          # short workspace
+    assert st != 0 and "workspace" in lib.moe_last_error().decode()
+    d2 = B.dims(2048, 512, 256, 4, 16, 1)
+    nout = (B.ctypes.byref(d2), fake, fake, fake, fake, None, B.ctypes.byref(ex), fake, fake, T,
+            None, fake, fake, fake, fake, float("nan"), fake, need, 0)
+    assert lib.moe_block_prefill(*nout) == 1                            # norm output with a NaN eps
+
+
 def test_expert_forward_validation(B):
     d = B.dims(2048, 512, 256, 4, 16, 1)
     fake = 1 << 40
