@@ -14,7 +14,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-def _layer(w, seed=0, scale_b=1.0):
+def _layer(w, seed=0):
     from int4_expert_ffn_int8_amd.layer import MoeLayer
     router = synth.router_tensors(w, 0, seed)
     experts = [synth.expert_tensors(w, 0, e, seed) for e in range(w["E"])]
@@ -158,3 +158,41 @@ def test_block_prefill_empty_batch_and_small_workspace():
     pb["ws"] = pb["ws"][:-256]
     with pytest.raises(B.MoeError):
         L.block_prefill(torch.zeros((T, w["H"]), dtype=torch.int16, device="cuda"), pb)
+
+
+def test_block_prefill_through_pool_matches_resident():
+    # moe_block_prefill with the routed experts behind a slot pool over a
+    # pinned host copy: cold (every expert read from the host copy, the down
+    # GEMM's output bound included) and warm give the resident bits
+    from int4_expert_ffn_int8_amd import binding as B
+    from int4_expert_ffn_int8_amd.layer import dev, pack_experts
+    w = synth.workload(0)
+    L, router, experts, shared = _layer(w, seed=21)
+    T = 300
+    xb = synth.tokens(w, 4, T=T, seed=21)
+    x = dev(xb)
+    pb0 = L.block_prefill_buffers(T)
+    L.block_prefill(x, pb0)
+    torch.cuda.synchronize()
+    out_res = pb0["out"].cpu().numpy().copy()
+    o_ref = O.moe_block(w, router, lambda e: experts[e], xb, shared=shared)
+    touched = np.unique(pb0["idx"].cpu().numpy()).astype(np.int32)
+    E, nb = w["E"], B.moe_expert_blob_bytes(w["H"], w["I"], w["r"])
+    host = torch.from_numpy(pack_experts(w["H"], w["I"], w["r"], experts)).pin_memory()
+    slots = torch.empty((1, 8, nb), dtype=torch.uint8, device="cuda")
+    table = torch.empty((1, E), dtype=torch.int32, device="cuda")
+    counters = torch.zeros(2, dtype=torch.int64, device="cuda")
+    pool = B.MoePool(1, E, 8, nb, slots, table, host)
+    try:
+        ex = pool.layer(0, counters)
+        for phase in ("cold", "warm"):
+            if phase == "warm":
+                pool.update(touched.reshape(1, -1))
+                pool.wait_layer(0)
+            pb = L.block_prefill_buffers(T)
+            L.block_prefill(x, pb, routed=ex)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(pb["out"].cpu().numpy(), out_res, err_msg=phase)
+        assert_bf16_output_close(out_res.view(np.uint16), o_ref, "pooled block prefill output")
+    finally:
+        pool.close()
