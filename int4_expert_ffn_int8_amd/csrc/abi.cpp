@@ -175,7 +175,8 @@ moe_status_t expert_forward(const moe_dims_t* d, const moe_experts_t* routed,
     int32_t* eh = reinterpret_cast<int32_t*>(wsb + W.eh);
     g.x16 = x16;
     g.ex = ex;
-    g.hf = reinterpret_cast<float*>(wsb + W.hf);
+    g.hl = reinterpret_cast<uint16_t*>(wsb + W.hl);
+    g.hbe = reinterpret_cast<int8_t*>(wsb + W.hbe);
     g.hmax = reinterpret_cast<uint32_t*>(wsb + W.hmax);
     g.hs = hs16;
     g.eh = eh;

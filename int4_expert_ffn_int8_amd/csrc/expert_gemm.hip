@@ -13,8 +13,10 @@
 //     [2^14, 2^15); the epilogue multiplies the row by 2^e.  Rows of x are
 //     converted once per token (k_x16_setup, whose last workgroup also does
 //     the per-group setup), rows of the SwiGLU output h once per row after
-//     the gate/up GEMM, from an fp32 h and its row maximum (by the LoRA-A
-//     GEMM of down, which reads every row of h anyway; by k_h16 without LoRA);
+//     the gate/up GEMM, from h stored by the gate/up epilogue as fp16 with
+//     one exponent per 16-column block and from its row maximum (by the
+//     LoRA-A GEMM of down, which reads every row of h anyway; by k_h16
+//     without LoRA): a power-of-two rescale of each block;
 //   * the unmerged LoRA delta ([P1] Recover-LoRA paragraph) is one extra
 //     64-wide K chunk on bf16 MFMA: the activation side holds
 //     lambda * (A v) * 2^-e as a bf16 hi + lo pair, the weight side holds B
@@ -145,24 +147,34 @@ __global__ void __launch_bounds__(256) k_x16_setup(X16SetupArgs a) {
   if (lane == 0) a.ex[t] = e;
 }
 
-// h [NR][I] fp32 -> hs16 [NR][I] fp16 scaled by 2^-eh[s], with the row maxima
-// hmax[s] (float bits of max |h|) from the gate/up epilogue.  One wave per
-// row, grid ceil(NR / 4), block 256.  Rows past `rows` (tiles that were not
+// h [NR][I] as fp16(h * 2^-hbe) per 16-column block -> hs16 [NR][I] fp16
+// scaled by 2^-eh[s] for the whole row, eh[s] from the row maxima hmax[s]
+// (float bits of max |h|) of the gate/up epilogue: a power-of-two rescale of
+// each block, exact unless a value becomes subnormal.  One wave per row,
+// grid ceil(NR / 4), block 256.  Rows past `rows` (tiles that were not
 // computed) are skipped.
-__global__ void __launch_bounds__(256) k_h16(const float* __restrict__ h, const uint32_t* __restrict__ hmax,
+__global__ void __launch_bounds__(256) k_h16(const uint16_t* __restrict__ hl, const int8_t* __restrict__ hbe,
+                                             const uint32_t* __restrict__ hmax,
                                              const int32_t* __restrict__ nrows, int I,
                                              uint16_t* __restrict__ hs16, int32_t* __restrict__ eh) {
   const int lane = threadIdx.x & 63;
   const int s = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (s >= *nrows) return;
   const int e = row_exp(__uint_as_float(hmax[s]));
-  const float4* src = reinterpret_cast<const float4*>(h + size_t(s) * I);
-  uint2* dst = reinterpret_cast<uint2*>(hs16 + size_t(s) * I);
-  for (int i = lane; i < I / 4; i += 64) {
-    const float4 v = src[i];
-    f16x2_t a = {_Float16(ldexpf(v.x, -e)), _Float16(ldexpf(v.y, -e))};
-    f16x2_t b = {_Float16(ldexpf(v.z, -e)), _Float16(ldexpf(v.w, -e))};
-    dst[i] = make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+  const uint4* src = reinterpret_cast<const uint4*>(hl + size_t(s) * I);
+  uint4* dst = reinterpret_cast<uint4*>(hs16 + size_t(s) * I);
+  for (int i = lane; i < I / 8; i += 64) {  // 8 columns, within one 16-column block
+    const uint4 v = src[i];
+    const int d = int(hbe[size_t(s) * (I / 16) + i / 2]) - e;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f16x2_t p = __builtin_bit_cast(f16x2_t, w[k]);
+      const f16x2_t r = {_Float16(ldexpf(float(p[0]), d)), _Float16(ldexpf(float(p[1]), d))};
+      o[k] = __builtin_bit_cast(uint32_t, r);
+    }
+    dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
   }
   if (lane == 0) eh[s] = e;
 }
@@ -544,24 +556,31 @@ __global__ void __launch_bounds__(512, 4) k_expert_gemm(GemmArgs a, int nblk) {
       const bool valid = s < row_end;
       const int e = row_e[m];
       if (MODE == kGemmGateUp) {
-        float hm = 0.f;
-#pragma unroll
-        for (int j = 0; j < JN; j += 2) {
-          const int Rg = n0 + wn0 + 16 * j + ln;  // gate blob row
-          const int jj = ((Rg >> 5) << 4) | (Rg & 15);
-          const float gv = ldexpf(acc[i][j][q], e);
-          // SiLU with the hardware exp and reciprocal (about 1e-6 relative);
-          // g -> -inf gives g * 0 = -0
-          const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * ldexpf(acc[i][j + 1][q], e);
-          if (valid && Rg < Nrows) a.hf[size_t(s) * a.I + jj] = hv;
-          if (Rg < Nrows) hm = fmaxf(hm, fabsf(hv));
-        }
-        // the 16 lanes of one row group hold the same row: one atomic per row
+        // the wave's gate/up columns 0..15 / 16..31 give the 16 h columns
+        // of one block (lane ln: column jj), stored as fp16(h * 2^-eb) with
+        // eb from the block's largest |h|; the row maximum over all blocks
+        // (an atomic per row) sets the exponent the down GEMM uses
+        static_assert(JN == 2, "one gate and one up column block per wave");
+        const int Rg = n0 + wn0 + ln;  // gate blob row
+        const int jj = ((Rg >> 5) << 4) | (Rg & 15);
+        const float gv = ldexpf(acc[i][0][q], e);
+        // SiLU with the hardware exp and reciprocal (about 1e-6 relative);
+        // g -> -inf gives g * 0 = -0
+        const float hv = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * ldexpf(acc[i][1][q], e);
+        float hm = Rg < Nrows ? fabsf(hv) : 0.f;
+        // the 16 lanes of one row group hold the same row
         hm = fmaxf(hm, dpp_f<kDppXor1>(hm));
         hm = fmaxf(hm, dpp_f<kDppXor2>(hm));
         hm = fmaxf(hm, dpp_f<kDppHalfMirror>(hm));
         hm = fmaxf(hm, dpp_f<kDppMirror>(hm));
-        if (valid && ln == 0) atomicMax(&a.hmax[s], __float_as_uint(hm));
+        const int eb = row_exp(hm);
+        if (valid && Rg < Nrows) {
+          a.hl[size_t(s) * a.I + jj] = __builtin_bit_cast(uint16_t, _Float16(ldexpf(hv, -eb)));
+          if (ln == 0) {
+            a.hbe[size_t(s) * (a.I / 16) + (jj >> 4)] = int8_t(eb);
+            atomicMax(&a.hmax[s], __float_as_uint(hm));
+          }
+        }
       } else if (a.y16 == nullptr) {
         const size_t dest = size_t(row_dst[m]);
         if (valid) {
@@ -603,9 +622,10 @@ hipError_t launch_x16_setup(const X16SetupArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_h16(const float* h, const uint32_t* hmax, const int32_t* nrows, int NR, int I,
-                      uint16_t* hs16, int32_t* eh, hipStream_t st) {
-  if (NR > 0) hipLaunchKernelGGL(k_h16, dim3((NR + 3) / 4), dim3(256), 0, st, h, hmax, nrows, I, hs16, eh);
+hipError_t launch_h16(const uint16_t* hl, const int8_t* hbe, const uint32_t* hmax, const int32_t* nrows,
+                      int NR, int I, uint16_t* hs16, int32_t* eh, hipStream_t st) {
+  if (NR > 0)
+    hipLaunchKernelGGL(k_h16, dim3((NR + 3) / 4), dim3(256), 0, st, hl, hbe, hmax, nrows, I, hs16, eh);
   return hipGetLastError();
 }
 

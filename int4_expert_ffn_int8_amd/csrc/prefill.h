@@ -32,7 +32,8 @@ struct GemmArgs {
   const uint16_t* x;          // [T][H] bf16
   const uint16_t* x16;        // [T][H] fp16 x * 2^-ex[t]
   const int32_t* ex;          // [T]
-  float* hf;                  // [NR][I] SwiGLU output h (fp32) in sorted rows
+  uint16_t* hl;               // [NR][I] SwiGLU output h as fp16(h * 2^-hbe) in sorted rows,
+  int8_t* hbe;                //   one exponent per 16-column block: hbe [NR][I/16]
   uint32_t* hmax;             // [NR] float bits of max |h| per row (zeroed by the setup)
   const uint16_t* hs;         // [NR][I] fp16 h * 2^-eh[s]
   const int32_t* eh;          // [NR]
@@ -85,8 +86,8 @@ struct X16SetupArgs {
   unsigned long long* gblob; // [E + 1]
 };
 hipError_t launch_x16_setup(const X16SetupArgs& a, hipStream_t st);
-hipError_t launch_h16(const float* h, const uint32_t* hmax, const int32_t* nrows, int NR, int I,
-                      uint16_t* hs16, int32_t* eh, hipStream_t st);
+hipError_t launch_h16(const uint16_t* hl, const int8_t* hbe, const uint32_t* hmax, const int32_t* nrows,
+                      int NR, int I, uint16_t* hs16, int32_t* eh, hipStream_t st);
 hipError_t launch_expert_gemm(int mode, const GemmArgs& a, int mtiles, hipStream_t st);
 
 }  // namespace moe

@@ -253,14 +253,12 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   // converted rows and exponents for the down GEMM as it goes: every row of
   // the sorted row space is read by exactly one workgroup, once.
   constexpr bool kH16 = (MODE == kLoraD);
-  const float* hrow[C::A_SEGS];
   int hexp[C::A_SEGS], hrs[C::A_SEGS];
 #pragma unroll
   for (int i = 0; i < C::A_SEGS; ++i) {
     const int s = row0 + ((tid + 256 * i) >> 3);
     const bool ok = kH16 && s < row_end;
     hrs[i] = ok ? s : -1;
-    hrow[i] = ok ? a.hf + size_t(s) * a.I : nullptr;
     hexp[i] = ok ? row_exp(__uint_as_float(a.hmax[s])) : 0;
   }
 
@@ -273,14 +271,15 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
     for (int j = 0; j < C::NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // register staging of a chunk, two chunks in flight (stages 0 and 1)
-  constexpr int H_SEGS = kH16 ? 2 * C::A_SEGS : 1;  // fp32 h segments (LoRA-A of down)
+  constexpr int H_SEGS = kH16 ? C::A_SEGS : 1;  // h segments with their block exponents (LoRA-A of down)
   // B staging: int4 -> 16B codes + scale/bias; int8 -> 16B codes; bf16 -> 16B
   constexpr int B_SEGS_INT8 = (BN * 4 + 255) / 256;   // 16B = 16 codes
   constexpr int B_SEGS_BF16 = (BN * 8 + 255) / 256;   // 16B = 8 bf16
   constexpr int B_SEGS = (MODE == kRouter) ? B_SEGS_INT8 : B_SEGS_BF16;
   struct Stage {
     uint4 ra[C::A_SEGS];
-    float4 rh[H_SEGS];
+    uint4 rh[H_SEGS];
+    int rhe[H_SEGS];
     uint4 rb[B_SEGS];
     float rs[B_SEGS];  // router: the fp32 group scale of the column
   };
@@ -295,15 +294,17 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
   // waits before a chunk's use cover only that chunk's loads.
   auto load_chunk = [&](Stage& st, int c) {
     uint4(&ra)[C::A_SEGS] = st.ra;
-    float4(&rh)[H_SEGS] = st.rh;
+    uint4(&rh)[H_SEGS] = st.rh;
+    int(&rhe)[H_SEGS] = st.rhe;
     uint4(&rb)[B_SEGS] = st.rb;
     const int k0 = c * BK;
     if constexpr (kH16) {
 #pragma unroll
       for (int i = 0; i < C::A_SEGS; ++i) {
-        const float* src = (hrow[i] ? hrow[i] : a.hf) + k0 + 8 * aseg[i];
-        rh[2 * i] = *reinterpret_cast<const float4*>(src);
-        rh[2 * i + 1] = *reinterpret_cast<const float4*>(src + 4);
+        const int s = hrs[i] >= 0 ? hrs[i] : 0;  // rows past the tile read row 0 (zeroed when stored)
+        const int col = k0 + 8 * aseg[i];        // 8 columns inside one 16-column block
+        rh[i] = *reinterpret_cast<const uint4*>(a.hl + size_t(s) * a.I + col);
+        rhe[i] = a.hbe[size_t(s) * (a.I / 16) + col / 16];
       }
     } else {
 #pragma unroll
@@ -351,23 +352,26 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
 
   auto store_chunk = [&](Stage& st, int c) {
     uint4(&ra)[C::A_SEGS] = st.ra;
-    float4(&rh)[H_SEGS] = st.rh;
+    uint4(&rh)[H_SEGS] = st.rh;
+    int(&rhe)[H_SEGS] = st.rhe;
     uint4(&rb)[B_SEGS] = st.rb;
-    if constexpr (kH16) {  // fp16(h * 2^-e), as the down GEMM reads it
+    if constexpr (kH16) {  // fp16(h * 2^-e), as the down GEMM reads it: a power-of-two rescale
 #pragma unroll
       for (int i = 0; i < C::A_SEGS; ++i) {
-        const int e = hexp[i];
-        const float4 v0 = rh[2 * i], v1 = rh[2 * i + 1];
-        const f16x2_t p0 = {_Float16(ldexpf(v0.x, -e)), _Float16(ldexpf(v0.y, -e))};
-        const f16x2_t p1 = {_Float16(ldexpf(v0.z, -e)), _Float16(ldexpf(v0.w, -e))};
-        const f16x2_t p2 = {_Float16(ldexpf(v1.x, -e)), _Float16(ldexpf(v1.y, -e))};
-        const f16x2_t p3 = {_Float16(ldexpf(v1.z, -e)), _Float16(ldexpf(v1.w, -e))};
-        ra[i] = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+        const int dd = rhe[i] - hexp[i];
+        const uint32_t hw[4] = {rh[i].x, rh[i].y, rh[i].z, rh[i].w};
+        uint32_t ow[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const f16x2_t p = __builtin_bit_cast(f16x2_t, hw[k]);
+          const f16x2_t r = {_Float16(ldexpf(float(p[0]), dd)), _Float16(ldexpf(float(p[1]), dd))};
+          ow[k] = __builtin_bit_cast(uint32_t, r);
+        }
+        ra[i] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
         ra[i] = and_mask(ra[i], hrs[i] >= 0);  // a row past the tile is zero
         if (hrs[i] >= 0) {
           *reinterpret_cast<uint4*>(a.hs_out + size_t(hrs[i]) * a.I + c * BK + 8 * aseg[i]) = ra[i];
-          if (c == 0 && aseg[i] == 0) a.eh_out[hrs[i]] = e;
+          if (c == 0 && aseg[i] == 0) a.eh_out[hrs[i]] = hexp[i];
         }
       }
     }
@@ -588,7 +592,7 @@ hipError_t launch_prefill_experts(const GemmArgs& a, const int32_t* counts, Expe
     ad.eh_out = eh;
     hipLaunchKernelGGL((k_gemm<kLoraD, kLoraBM, 64, 2, 2>), dim3(mt * (kPrefillBM / kLoraBM)), dim3(256), 0, st, ad);
   } else {
-    e = launch_h16(a.hf, a.hmax, a.gstart + a.E + 1, NR, a.I, hs16, eh, st);
+    e = launch_h16(a.hl, a.hbe, a.hmax, a.gstart + a.E + 1, NR, a.I, hs16, eh, st);
     if (e != hipSuccess) return e;
   }
   return launch_expert_gemm(kGemmDown, a, mt, st);

@@ -27,7 +27,8 @@ struct WsLayout {
   size_t upart;       // fp32 [kLoraSplit, NR, 32] K-split partials of the gate/up LoRA-A
   size_t x16;         // fp16 [T, H]    x * 2^-ex (prefill)
   size_t ex;          // int32 [T]
-  size_t hf;          // fp32 [NR, I]   h in sorted rows
+  size_t hl;          // fp16 [NR, I]   h in sorted rows, scaled per 16-column block
+  size_t hbe;         // int8 [NR, I/16] the blocks' exponents
   size_t hmax;        // u32 [NR]       max |h| per row
   size_t hs16;        // fp16 [NR, I]   h * 2^-eh
   size_t eh;          // int32 [NR]
@@ -60,7 +61,8 @@ inline WsLayout ws_layout(const moe_dims_t& d, int T, bool prefill) {
   const size_t TP = prefill ? size_t(T) : 0;
   W.x16 = o;        o = align256(o + TP * d.H * 2);
   W.ex = o;         o = align256(o + TP * 4);
-  W.hf = o;         o = align256(o + NR * d.I * 4);
+  W.hl = o;         o = align256(o + NR * d.I * 2);
+  W.hbe = o;        o = align256(o + NR * (d.I / 16));
   W.hmax = o;       o = align256(o + NR * 4);
   W.hs16 = o;       o = align256(o + NR * d.I * 2);
   W.eh = o;         o = align256(o + NR * 4);
