@@ -76,7 +76,7 @@ __global__ void __launch_bounds__(256) k_router_logits(const int8_t* __restrict_
   }
 }
 
-constexpr int kMaxTopkSplits = 4;  // K splits of the router GEMM summed by k_topk
+constexpr int kMaxTopkSplits = kRouterSplit;  // K splits of the router GEMM summed by k_topk
 
 constexpr int kTopkTokens = 16;  // tokens (waves) per top-K workgroup
 
