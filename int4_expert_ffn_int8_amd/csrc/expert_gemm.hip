@@ -542,7 +542,8 @@ __global__ void __launch_bounds__(512, 4) k_expert_gemm(GemmArgs a, int nblk) {
   if (MODE == kGemmDown && a.y16 != nullptr) {
     const float* meta = reinterpret_cast<const float*>(blob + a.L.meta);
     const float bound = gload<float>(meta + kMetaDownW) + fabsf(a.lam) * gload<float>(meta + kMetaDownL);
-    yc = !(bound > 0.f) ? 0 : (bound <= 3.0e38f ? min(ilogbf(bound) + 1, 127) : 127);
+    // (c >= -126 keeps 2^-c finite; a smaller bound still gives |acc| 2^-c < 2^15)
+    yc = !(bound > 0.f) ? 0 : (bound <= 3.0e38f ? max(min(ilogbf(bound) + 1, 127), -126) : 127);
     yscale = ldexpf(1.0f, -yc);
   }
 
