@@ -46,6 +46,8 @@ FUSED = [
     (2048, 2048, 16, 12, 3, 1, 2),   # the largest H and I together
     (256, 256, 8, 8, 2, 0, 4),       # four tokens, no shared expert
     (2048, 128, 4, 16, 4, 1, 1),     # the narrowest I under the widest H (r <= I / 32)
+    (512, 512, 16, 16, 1, 1, 3),     # K = 1 with a shared expert, three tokens
+    (1024, 512, 16, 32, 1, 0, 4),    # K = 1 alone, four tokens
 ]
 
 
